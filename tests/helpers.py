@@ -1,0 +1,65 @@
+"""Test helpers: run a workloads.Case through the oracle, compare results.
+
+Everything here is test infrastructure; expected values come only from the
+oracle (or from the pages' printed numbers), never from the HIP library.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import workloads
+
+
+def oracle_slots(orc, case) -> np.ndarray:
+    """slot_mapping for the case's new tokens (-1 where a sequence has no token)."""
+    pos = case.new_pos
+    ok = pos >= 0
+    slots = np.full(pos.shape, -1, dtype=np.int32)
+    if ok.any():
+        slots[ok] = orc.resolve_slots(case.block_table, case.block_size, case.num_blocks,
+                                      case.new_batch_idx[ok], pos[ok])
+    return slots
+
+
+def oracle_write(orc, case, slots) -> None:
+    """Write the case's new rows into its own caches (in place)."""
+    orc.cache_write(case.k_cache, slots, case.new_k)
+    if case.v_cache is not None:
+        orc.cache_write(case.v_cache, slots, case.new_v)
+    if case.k_rope_cache is not None:
+        orc.cache_write(case.k_rope_cache, slots, case.new_k_rope)
+
+
+def oracle_attend(orc, case, units=None, want_probs=False, nthreads=0):
+    if case.kind == "decode":
+        return orc.paged_decode(case.q, case.k_cache, case.v_cache_or_k, case.block_table,
+                                case.seq_lens, case.scale, case.window, q_rope=case.q_rope,
+                                k_rope_cache=case.k_rope_cache, units=units,
+                                want_probs=want_probs, nthreads=nthreads)
+    return orc.paged_prefill(case.q, case.k_cache, case.v_cache_or_k, case.block_table,
+                             case.cu_seqlens_q, case.seq_lens, case.scale, case.window,
+                             q_rope=case.q_rope, k_rope_cache=case.k_rope_cache, units=units,
+                             want_probs=want_probs, nthreads=nthreads)
+
+
+def oracle_run(orc, case, units=None, want_probs=False, inplace=False, nthreads=0):
+    """resolve -> write -> attend on the CPU.  Returns (out, written_case, slots)."""
+    c = case if inplace else case.copy_caches()
+    slots = oracle_slots(orc, c)
+    oracle_write(orc, c, slots)
+    out = oracle_attend(orc, c, units=units, want_probs=want_probs, nthreads=nthreads)
+    return out, c, slots
+
+
+def round_like_output(ref: np.ndarray, out_dtype: str) -> np.ndarray:
+    """The oracle's float64 result expressed in the output dtype (RNE), as float64."""
+    if out_dtype == "bf16":
+        return workloads.bf16_to_f32(workloads.bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    return ref.astype(np.float32).astype(np.float64)
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per output row (last axis): ||got - ref||_2 / ||ref||_2 (0 where both rows are 0)."""
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
