@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV-cache hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input, all
+on the GPU through the C ABI:
+    pkv_resolve_slots (new tokens' slots through the block table)
+    -> kv_cache_write (scatter the new K/V rows into the paged cache)
+    -> paged_attn_decode (split-K decode + combine) / paged_attn_prefill.
+Inputs are resident in HBM before the timed region.  Prints ONE JSON line.
+
+Default workload: llama2-7B-shaped single-layer MHA decode (B=64, H=H_kv=32,
+d=128, every length 2048, bf16, 1024-block shuffled pool).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, published
+METRIC = "paged decode KV GB/s (% of HBM peak) + tokens/s; prefill MFMA util"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mha_decode_7b")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--split-tokens", type=int, default=0, help="decode partition size (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    return ap.parse_args()
+
+
+def _dev(torch, a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def algorithmic_bytes(case):
+    """Bytes the method must move per step, by call: (resolve, write, attention)."""
+    eb = 2 if case.dtype == "bf16" else 4
+    L = case.seq_lens.astype(np.int64)
+    T = case.new_pos.size
+    resolve = T * 16  # batch index, position, table entry, slot
+    row = case.Hkv * case.D * eb
+    write = T * (4 + 2 * row * (1 if case.is_mla else 2) + (2 * case.Hkv * case.rope_dim * eb))
+    if case.kind == "decode":
+        lo = np.maximum(0, L - case.window) if case.window else np.zeros_like(L)
+        keys = L - lo
+        blocks = np.where(L > 0, (L - 1) // case.block_size - lo // case.block_size + 1, 0)
+        q_rows = case.B * case.H
+    else:
+        keys = L
+        blocks = -(-L // case.block_size)
+        q_rows = case.q.shape[0] * case.H
+    if case.is_mla:  # latent read once serves as key and value; rope part beside it
+        kv = int(keys.sum()) * (case.D + case.rope_dim) * eb
+    else:
+        kv = int(keys.sum()) * case.Hkv * 2 * case.D * eb
+    qo = q_rows * (case.D + case.rope_dim) * eb + q_rows * case.D * eb
+    attn = kv + qo + int(blocks.sum()) * 4 + case.B * 4
+    return resolve, write, attn, kv
+
+
+def cpu_baseline(case, target_s):
+    """The oracle, as it stands, on the host cores: whole steps of the same workload."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from helpers import oracle_run
+
+    oracle.build()
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle_run(oracle, case, inplace=True)
+    one = time.perf_counter() - t0
+    reps = max(1, int(target_s / max(one, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle_run(oracle, case, inplace=True)
+    el = (time.perf_counter() - t0) / reps
+    r, w, a, _ = algorithmic_bytes(case)
+    return {"value": round((r + w + a) / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} whole steps (resolve + write + attention of all {case.B * case.H} rows) of "
+                      f"{case.name} seed {case.seed_label}, {el * 1e3:.1f} ms per step, fp64, {threads} threads",
+            "ms_per_step": round(el * 1e3, 3)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this build "
+              "(sharding is described in DESIGN.md, not run)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_80_amd as pkv
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    pkv.load()
+
+    case = workloads.WORKLOADS[args.workload](args.seed)
+    case.seed_label = args.seed
+    dev = lambda a: _dev(torch, a)  # noqa: E731
+    cache = pkv.PagedKVCache(dev(case.k_cache), dev(case.v_cache), dev(case.k_rope_cache))
+    bt, sl = dev(case.block_table), dev(case.seq_lens)
+    q, q_rope = dev(case.q), dev(case.q_rope)
+    new_k, new_v, new_kr = dev(case.new_k), dev(case.new_v), dev(case.new_k_rope)
+    bidx, pos = dev(case.new_batch_idx), dev(case.new_pos)
+    slots = torch.empty(case.new_pos.size, dtype=torch.int32, device="cuda")
+    out = torch.empty((case.q.shape[0], case.H, case.D), dtype=q.dtype, device="cuda")
+    if case.kind == "decode":
+        ws_bytes = pkv.paged_attn_decode_workspace(cache, case.B, case.H, case.max_blocks, case.scale,
+                                                   case.window, pkv.PKV_BF16 if case.dtype == "bf16" else pkv.PKV_F32,
+                                                   args.split_tokens)
+    else:
+        ws_bytes = 0
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    max_q = int(np.diff(case.cu_seqlens_q).max(initial=0)) if case.kind == "prefill" else 1
+    cu = dev(case.cu_seqlens_q)
+
+    def attend():
+        if case.kind == "decode":
+            pkv.paged_attn_decode(q, cache, bt, sl, case.scale, case.window, q_rope=q_rope, out=out,
+                                  split_tokens=args.split_tokens, workspace=ws)
+        else:
+            pkv.paged_attn_prefill(q, cache, bt, cu, sl, max_q, case.scale, case.window, q_rope=q_rope,
+                                   out=out, workspace=ws)
+
+    def step(e0=None, e1=None):
+        pkv.pkv_resolve_slots(bt, case.block_size, bidx, pos, slots_out=slots)
+        pkv.kv_cache_write(slots, new_k, new_v, cache, k_rope=new_kr)
+        if e0 is not None:
+            e0.record()
+        attend()
+        if e1 is not None:
+            e1.record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for e0, e1 in ev:
+        step(e0, e1)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    ms_attn = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    r_b, w_b, a_b, kv_b = algorithmic_bytes(case)
+    step_bytes = r_b + w_b + a_b
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    attn_gbs = a_b / (ms_attn * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {"workload": case.name, "batch": case.B, "num_q_heads": case.H, "num_kv_heads": case.Hkv,
+                   "head_dim": case.D, "rope_dim": case.rope_dim, "block_size": case.block_size,
+                   "window": case.window, "seq_len_total": int(case.seq_lens.sum()), "seed": args.seed},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(case.new_pos.size / (ms_step * 1e-3), 1),
+        "attention_ms": round(ms_attn, 4),
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attn_decode" if case.kind == "decode" else "paged_attn_prefill",
+                     "bytes_per_launch": a_b},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

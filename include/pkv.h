@@ -1,0 +1,154 @@
+/*
+ * pkv.h -- C ABI of the MI355X (gfx950) paged-KV-cache attention library (libpkv.so).
+ *
+ * The cache of one layer is stored in fixed-size blocks:
+ *     k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim]
+ * and a logical (sequence b, position p) lives at the physical slot
+ *     block_table[b][p / block_size] * block_size + p % block_size
+ * (the layout and address map of the "KVCache optimisation skill" page,
+ * mode 2 and section 3.1, and of the "Ascend NPU standalone-deployment
+ * KVCache guide", mode 2).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers to dense row-major arrays that the
+ *     caller owns.  The library never allocates, frees or synchronises; it
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the default stream)
+ *     and returns.  Scratch memory comes from the caller as `workspace`.
+ *   - Index arrays (block_table, slot_mapping, seq_lens, cu_seqlens_q,
+ *     batch_idx, pos) are int32 (the skill page's notes require an int32
+ *     block table).
+ *   - Element arrays are float32 or bfloat16, one dtype per call; there is no
+ *     implicit conversion.  Every element base pointer must be 16-byte aligned.
+ *   - Only host-visible arguments are validated (pointers, sizes, shapes,
+ *     dtypes, scale, workspace size).  A failed check returns a non-zero
+ *     status, launches nothing and leaves a message for pkv_last_error().
+ *     The CONTENTS of device index arrays are trusted: a block id outside
+ *     [0, num_blocks), a sequence length beyond max_blocks_per_seq *
+ *     block_size or a slot outside the cache is undefined behaviour.
+ *   - Launch failures return PKV_ERR_HIP.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* a host-visible argument is malformed                 */
+  PKV_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels implement  */
+  PKV_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace size  */
+  PKV_ERR_HIP = 4          /* a HIP launch or runtime call failed                  */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* One layer's paged cache.  Standard attention: k_cache and v_cache of width
+ * head_dim, k_rope_cache NULL, rope_dim 0.  MLA absorbed form ("KVCache
+ * optimisation skill", mode 3): k_cache holds the latent (cache_nope, width
+ * head_dim = kv_lora_rank = 512), v_cache must be the SAME pointer (key =
+ * value = cache_nope), k_rope_cache holds the rotary part (cache_rope,
+ * [num_blocks, block_size, 1, rope_dim] with rope_dim = 64) and
+ * num_kv_heads = 1 -- the constraints that page lists for this mode. */
+typedef struct {
+  void* k_cache;
+  void* v_cache;
+  void* k_rope_cache;
+  int32_t num_blocks;
+  int32_t block_size;   /* tokens per block: 16, 32, 64 or 128                       */
+  int32_t num_kv_heads;
+  int32_t head_dim;     /* 64, 128 or 256; 512 for MLA                                */
+  int32_t rope_dim;     /* 0, or 64 for MLA                                           */
+  int32_t dtype;        /* pkv_dtype of every cache tensor and of q / k / v / q_rope */
+} pkv_paged_cache;
+
+/* Attention parameters.  There are no defaults: a zero or negative scale is an
+ * error (the Ascend guide's FA v1/v2 name table warns that a misnamed scale
+ * silently becomes 1.0). */
+typedef struct {
+  int32_t batch;              /* number of sequences B                                       */
+  int32_t num_q_heads;        /* H; H % num_kv_heads == 0; query head h reads KV head h / (H / H_kv) */
+  int32_t max_blocks_per_seq; /* row stride of block_table                                   */
+  float scale;                /* softmax scale, finite and > 0 (1/sqrt(d) in the pages)      */
+  int32_t window;             /* 0 = full attention; W > 0: a query at position p sees keys  */
+                              /* p-W < j <= p ("KV Cache notes", sliding-window section)     */
+  int32_t out_dtype;          /* pkv_dtype of `out` (f32 out is a diagnostic mode)           */
+  int32_t split_tokens;       /* decode only: keys per workgroup partition, a multiple of    */
+                              /* block_size; 0 = chosen by the library                       */
+} pkv_attn_params;
+
+/* slots_out[i] = block_table[batch_idx[i]][pos[i] / block_size] * block_size + pos[i] % block_size
+ * for i < n ("KVCache optimisation skill", section 3.1; the framework's
+ * prepare_slot_mapping of the KV Cache management design document).
+ * block_table: [batch, max_blocks_per_seq]; batch_idx, pos, slots_out: [n].
+ * A negative pos gives slot -1 (a row kv_cache_write skips). */
+pkv_status pkv_resolve_slots(const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                             int32_t block_size, const int32_t* batch_idx, const int32_t* pos,
+                             int32_t n, int32_t* slots_out, void* stream);
+
+/* Cache write ("Ascend NPU standalone-deployment KVCache guide", mode 2: the
+ * scatter into the cache viewed as [num_blocks*block_size, num_kv_heads, head_dim]).
+ * Row t of k (and v, and k_rope) is copied bit for bit to cache row slot_mapping[t].
+ *   slot_mapping : [num_tokens]; a negative slot skips the row.  Slots must be distinct.
+ *   k, v         : [num_tokens, num_kv_heads, head_dim]; v must be NULL when
+ *                  cache->v_cache == cache->k_cache (MLA latent written once)
+ *   k_rope       : [num_tokens, num_kv_heads, rope_dim] iff cache->rope_dim > 0, else NULL */
+pkv_status kv_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const void* k,
+                          const void* v, const void* k_rope, const pkv_paged_cache* cache,
+                          void* stream);
+
+/* Bytes of workspace paged_attn_decode needs for these arguments (0 is possible). */
+size_t paged_attn_decode_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache);
+
+/* Decode (q_len = 1): out[b, h] = softmax(q[b,h] . K_b^T * scale) V_b over the keys of
+ * sequence b visible to its newest position ("KV Cache notes": the attention
+ * formula and its decode form; sparse_mode 0 of the skill page's appendix C).
+ *   q            : [batch, H, head_dim];  q_rope: [batch, H, rope_dim] iff MLA, else NULL
+ *   block_table  : [batch, max_blocks_per_seq]
+ *   seq_lens     : [batch], valid keys of each sequence INCLUDING the token written
+ *                  this step (the query sits at position seq_lens[b]-1); 0 gives a zero row
+ *   out          : [batch, H, head_dim] in params->out_dtype
+ *   workspace    : >= paged_attn_decode_workspace(params, cache) bytes of device memory
+ * With a window, table entries for blocks wholly before the window are never read
+ * (they may hold the null block, as the KV Cache management design document's
+ * sliding-window manager lays them out). */
+pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_cache* cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             const pkv_attn_params* params, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace paged_attn_prefill needs (0 is possible). */
+size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache,
+                                    int32_t total_q);
+
+/* Chunked causal prefill over an existing paged cache (sparse_mode 3 of the skill
+ * page's appendix C, bottom-right aligned as in the "KV Cache notes" minimal
+ * implementation): new row i of sequence b sits at position seq_lens_kv[b] - n_b + i
+ * and sees keys j <= that position (and > position - window when window > 0).
+ *   q            : TND [total_q, H, head_dim]; q_rope: [total_q, H, rope_dim] iff MLA
+ *   cu_seqlens_q : [batch + 1], cu[0] = 0, cu[batch] = total_q, n_b = cu[b+1] - cu[b] >= 0
+ *   seq_lens_kv  : [batch], cached + new keys (n_b <= seq_lens_kv[b]); the new rows
+ *                  must already be in the cache (kv_cache_write first)
+ *   max_q_len    : an upper bound of every n_b (sizes the grid)
+ *   out          : [total_q, H, head_dim] in params->out_dtype */
+pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged_cache* cache,
+                              const int32_t* block_table, const int32_t* cu_seqlens_q,
+                              const int32_t* seq_lens_kv, int32_t total_q, int32_t max_q_len,
+                              const pkv_attn_params* params, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

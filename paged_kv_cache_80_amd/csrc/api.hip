@@ -1,0 +1,275 @@
+// api.hip -- the C ABI of libpkv (declared in include/pkv.h): argument checks,
+// partition sizing and kernel launches on the caller's stream.  No allocation,
+// no synchronisation, no device reads on the host side.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "device_common.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+pkv_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t d) { return d == PKV_F32 || d == PKV_BF16; }
+
+bool pow2_block(int32_t bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
+
+int32_t log2i(int32_t v) { return __builtin_ctz((unsigned)v); }
+
+bool is_mla(const pkv_paged_cache* c) { return c->rope_dim > 0; }
+
+// Shared structural checks of a cache description.
+pkv_status check_cache(const pkv_paged_cache* c) {
+  if (!c) return fail(PKV_ERR_INVALID_ARG, "cache is NULL");
+  if (!c->k_cache || !c->v_cache) return fail(PKV_ERR_INVALID_ARG, "k_cache / v_cache is NULL");
+  if (!valid_dtype(c->dtype)) return fail(PKV_ERR_INVALID_ARG, "cache dtype %d is not f32 or bf16", c->dtype);
+  if (c->num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks %d must be > 0", c->num_blocks);
+  if (!pow2_block(c->block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not one of 16, 32, 64, 128", c->block_size);
+  if (c->num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads %d must be > 0", c->num_kv_heads);
+  if (c->head_dim <= 0) return fail(PKV_ERR_INVALID_ARG, "head_dim %d must be > 0", c->head_dim);
+  if (c->rope_dim < 0) return fail(PKV_ERR_INVALID_ARG, "rope_dim %d must be >= 0", c->rope_dim);
+  if ((c->rope_dim > 0) != (c->k_rope_cache != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_rope_cache must be given exactly when rope_dim > 0");
+  const int64_t row = (int64_t)c->num_kv_heads * c->head_dim * elem_bytes(c->dtype);
+  if (row % 16 != 0) return fail(PKV_ERR_UNSUPPORTED, "a cache row of %lld bytes is not a multiple of 16", (long long)row);
+  if (c->rope_dim > 0 && ((int64_t)c->num_kv_heads * c->rope_dim * elem_bytes(c->dtype)) % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "a rope row is not a multiple of 16 bytes");
+  if (!aligned16(c->k_cache) || !aligned16(c->v_cache) || (c->k_rope_cache && !aligned16(c->k_rope_cache)))
+    return fail(PKV_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+  if (is_mla(c)) {
+    // "KVCache optimisation skill", mode 3 constraints: key = value = cache_nope,
+    // rope D = 64, latent width 512, a single latent head.
+    if (c->v_cache != c->k_cache) return fail(PKV_ERR_INVALID_ARG, "MLA: v_cache must alias k_cache (key = value = cache_nope)");
+    if (c->rope_dim != 64) return fail(PKV_ERR_UNSUPPORTED, "MLA: rope_dim must be 64 (got %d)", c->rope_dim);
+    if (c->num_kv_heads != 1) return fail(PKV_ERR_INVALID_ARG, "MLA: num_kv_heads must be 1 (got %d)", c->num_kv_heads);
+    if (c->head_dim != 512) return fail(PKV_ERR_UNSUPPORTED, "MLA: latent width must be 512 (got %d)", c->head_dim);
+  }
+  return PKV_OK;
+}
+
+pkv_status check_params(const pkv_attn_params* p, const pkv_paged_cache* c) {
+  if (!p) return fail(PKV_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch %d must be >= 0", p->batch);
+  if (p->batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch %d exceeds 65535", p->batch);
+  if (p->num_q_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d must be > 0", p->num_q_heads);
+  if (p->num_q_heads % c->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", p->num_q_heads,
+                c->num_kv_heads);
+  if (p->max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0");
+  if (!(std::isfinite(p->scale) && p->scale > 0.f))
+    return fail(PKV_ERR_INVALID_ARG, "scale %g must be finite and > 0 (there is no default)", (double)p->scale);
+  if (p->window < 0) return fail(PKV_ERR_INVALID_ARG, "window %d must be >= 0", p->window);
+  if (!valid_dtype(p->out_dtype)) return fail(PKV_ERR_INVALID_ARG, "out_dtype %d is not f32 or bf16", p->out_dtype);
+  if (p->split_tokens < 0 || (p->split_tokens % c->block_size) != 0)
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d must be a non-negative multiple of block_size %d",
+                p->split_tokens, c->block_size);
+  return PKV_OK;
+}
+
+// Decode partitioning: blocks per partition and the partition count bound.
+struct DecodePlan {
+  int32_t bpp;
+  int32_t max_np;
+  size_t ws_bytes;
+  size_t ws_ml_offset;
+};
+
+constexpr int32_t kMaxBpp = 1024;
+
+DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
+  const int32_t bs = c->block_size;
+  int32_t span = p->max_blocks_per_seq;  // table blocks one sequence can touch
+  if (p->window > 0) span = std::min<int64_t>(span, (p->window + bs - 1) / bs + 1);
+  int32_t bpp;
+  if (p->split_tokens > 0) {
+    bpp = p->split_tokens / bs;
+  } else {
+    // Enough workgroups to fill 256 CUs several times, partitions of at most a
+    // few hundred KiB so ragged lengths balance.
+    const int64_t units = (int64_t)p->batch * c->num_kv_heads;
+    const int32_t part_tokens = units >= 1024 ? 2048 : 512;
+    bpp = std::max(1, part_tokens / bs);
+  }
+  bpp = std::max(1, std::min({bpp, span, kMaxBpp}));
+  DecodePlan plan;
+  plan.bpp = bpp;
+  plan.max_np = (span + bpp - 1) / bpp;
+  plan.ws_bytes = 0;
+  plan.ws_ml_offset = 0;
+  if (plan.max_np > 1) {
+    const size_t rows = (size_t)p->batch * p->num_q_heads * plan.max_np;
+    const size_t o_bytes = (rows * c->head_dim * sizeof(float) + 255) & ~size_t(255);
+    plan.ws_ml_offset = o_bytes;
+    plan.ws_bytes = o_bytes + rows * 2 * sizeof(float);
+  }
+  return plan;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+pkv_status pkv_resolve_slots(const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                             int32_t block_size, const int32_t* batch_idx, const int32_t* pos, int32_t n,
+                             int32_t* slots_out, void* stream) {
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n %d must be >= 0", n);
+  if (n == 0) return ok();
+  if (!block_table || !batch_idx || !pos || !slots_out) return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if (batch <= 0 || max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "batch and max_blocks_per_seq must be > 0");
+  if (!pow2_block(block_size)) return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not one of 16, 32, 64, 128", block_size);
+  return from_hip(pkv::launch_resolve_slots(block_table, batch, max_blocks_per_seq, block_size, batch_idx, pos, n,
+                                            slots_out, static_cast<hipStream_t>(stream)),
+                  "pkv_resolve_slots launch");
+}
+
+pkv_status kv_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const void* k, const void* v,
+                          const void* k_rope, const pkv_paged_cache* cache, void* stream) {
+  pkv_status s = check_cache(cache);
+  if (s) return s;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %d must be >= 0", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!slot_mapping || !k) return fail(PKV_ERR_INVALID_ARG, "slot_mapping and k must not be NULL");
+  const bool shared_kv = cache->v_cache == cache->k_cache;
+  if (shared_kv && v) return fail(PKV_ERR_INVALID_ARG, "v must be NULL when v_cache aliases k_cache");
+  if (!shared_kv && !v) return fail(PKV_ERR_INVALID_ARG, "v must not be NULL");
+  if ((cache->rope_dim > 0) != (k_rope != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_rope must be given exactly when the cache has a rope part");
+  if (!aligned16(k) || (v && !aligned16(v)) || (k_rope && !aligned16(k_rope)))
+    return fail(PKV_ERR_INVALID_ARG, "k / v / k_rope must be 16-byte aligned");
+  pkv::WriteRows rows{};
+  const int32_t eb = elem_bytes(cache->dtype);
+  rows.src[0] = k;
+  rows.dst[0] = cache->k_cache;
+  rows.row_bytes[0] = cache->num_kv_heads * cache->head_dim * eb;
+  rows.count = 1;
+  if (!shared_kv) {
+    rows.src[1] = v;
+    rows.dst[1] = cache->v_cache;
+    rows.row_bytes[1] = rows.row_bytes[0];
+    rows.count = 2;
+  }
+  if (cache->rope_dim > 0) {
+    rows.src[rows.count] = k_rope;
+    rows.dst[rows.count] = cache->k_rope_cache;
+    rows.row_bytes[rows.count] = cache->num_kv_heads * cache->rope_dim * eb;
+    rows.count++;
+  }
+  return from_hip(pkv::launch_cache_write(slot_mapping, num_tokens, rows, static_cast<hipStream_t>(stream)),
+                  "kv_cache_write launch");
+}
+
+size_t paged_attn_decode_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache) {
+  if (check_cache(cache) || check_params(params, cache)) return 0;
+  return plan_decode(params, cache).ws_bytes;
+}
+
+pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_cache* cache,
+                             const int32_t* block_table, const int32_t* seq_lens, const pkv_attn_params* params,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  pkv_status s = check_cache(cache);
+  if (s) return s;
+  s = check_params(params, cache);
+  if (s) return s;
+  if (params->batch == 0) return ok();
+  if (!q || !block_table || !seq_lens || !out) return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((q_rope != nullptr) != is_mla(cache))
+    return fail(PKV_ERR_INVALID_ARG, "q_rope and k_rope must be given together or not at all");
+  if (!aligned16(q) || !aligned16(out) || (q_rope && !aligned16(q_rope)))
+    return fail(PKV_ERR_INVALID_ARG, "q / q_rope / out must be 16-byte aligned");
+  const int32_t group = params->num_q_heads / cache->num_kv_heads;
+  const DecodePlan plan = plan_decode(params, cache);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (plan.ws_bytes > 0 && !aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (is_mla(cache)) return fail(PKV_ERR_UNSUPPORTED, "MLA decode is not built yet");
+  if (!pkv::decode_valu_supported(cache->dtype, cache->head_dim, group))
+    return fail(PKV_ERR_UNSUPPORTED, "decode: dtype %d, head_dim %d, group %d not supported", cache->dtype,
+                cache->head_dim, group);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.ws_o = plan.max_np > 1 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = plan.max_np > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset) : nullptr;
+  a.batch = params->batch;
+  a.num_q_heads = params->num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.max_blocks_per_seq = params->max_blocks_per_seq;
+  a.block_size_log2 = log2i(cache->block_size);
+  a.blocks_per_part = plan.bpp;
+  a.max_np = plan.max_np;
+  a.window = params->window;
+  a.scale_log2e = params->scale * pkv::kLog2e;
+  a.dtype = cache->dtype;
+  a.out_dtype = params->out_dtype;
+  hipError_t e = pkv::launch_decode_valu(a, st);
+  if (e != hipSuccess) return from_hip(e, "decode launch");
+  if (plan.max_np > 1) {
+    e = pkv::launch_decode_combine(a.ws_o, a.ws_ml, seq_lens, params->batch, params->num_q_heads, cache->head_dim,
+                                   plan.max_np, a.block_size_log2, plan.bpp, params->window, out,
+                                   params->out_dtype, st);
+    if (e != hipSuccess) return from_hip(e, "decode combine launch");
+  }
+  return ok();
+}
+
+size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache, int32_t total_q) {
+  (void)params;
+  (void)cache;
+  (void)total_q;
+  return 0;
+}
+
+pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged_cache* cache,
+                              const int32_t* block_table, const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,
+                              int32_t total_q, int32_t max_q_len, const pkv_attn_params* params, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  (void)q, (void)q_rope, (void)block_table, (void)cu_seqlens_q, (void)seq_lens_kv, (void)total_q,
+      (void)max_q_len, (void)out, (void)workspace, (void)workspace_bytes, (void)stream;
+  pkv_status s = check_cache(cache);
+  if (s) return s;
+  s = check_params(params, cache);
+  if (s) return s;
+  return fail(PKV_ERR_UNSUPPORTED, "prefill is not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// pkv_internal.h -- host-side declarations shared by the C-ABI layer and the kernel
+// translation units of libpkv.  Not installed; the public interface is include/pkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Index resolution and cache write (write.hip).
+hipError_t launch_resolve_slots(const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                                int32_t block_size, const int32_t* batch_idx, const int32_t* pos,
+                                int32_t n, int32_t* slots_out, hipStream_t stream);
+
+// rows: up to three source/destination pairs copied per token (K, V, rope).
+struct WriteRows {
+  const void* src[3];
+  void* dst[3];
+  int32_t row_bytes[3];
+  int32_t count;
+};
+hipError_t launch_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const WriteRows& rows,
+                              hipStream_t stream);
+
+// Split-K decode on the vector ALUs (decode.hip).
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;
+  float* ws_o;   // [B*H, max_np, D] partial outputs (unnormalised), or null when max_np == 1
+  float* ws_ml;  // [B*H, max_np, 2] running max (log2 domain) and sum
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  int32_t max_blocks_per_seq, block_size_log2;
+  int32_t blocks_per_part, max_np;
+  int32_t window;
+  float scale_log2e;
+  int32_t dtype, out_dtype;
+};
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
+bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);
+
+// Second pass of split-K decode: merges the partitions of each (sequence, head).
+hipError_t launch_decode_combine(const float* ws_o, const float* ws_ml, const int32_t* seq_lens,
+                                 int32_t batch, int32_t num_q_heads, int32_t v_dim, int32_t max_np,
+                                 int32_t block_size_log2, int32_t blocks_per_part, int32_t window,
+                                 void* out, int32_t out_dtype, hipStream_t stream);
+
+}  // namespace pkv

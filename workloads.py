@@ -9,8 +9,9 @@ and the HIP library, independently).
 Draw order for every case (fixed, so a seed names one input):
     seq_lens -> block permutation -> q (-> q_rope) -> cache pool -> new k, v (-> k_rope)
 
-Values are N(0, 1) float32; bf16 cases round them to bfloat16 by
-round-to-nearest-even and store the raw uint16 bits.
+Values are N(0, 1) float32 (see Draws for how each array's stream is laid
+out); bf16 cases round them to bfloat16 by round-to-nearest-even and store
+the raw uint16 bits.
 
 Shapes follow the pages' workloads: the 2-batch / 128-token-block layout of the
 skill page's section 3.1, llama2-7B (MHA 32 heads) and llama2-70B (GQA 64/8)
@@ -19,8 +20,10 @@ head geometry from the "KV Cache notes" accounting table, and the MLA latent
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -41,10 +44,7 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def normal(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 26) -> np.ndarray:
-    """N(0,1) values of the given shape: float32 array or bf16 raw bits (uint16).
-
-    Large arrays are drawn in chunks (same stream order as one draw of the
-    flattened array, chunk by chunk) so the float32 staging stays bounded."""
+    """N(0,1) values of the given shape from one generator: float32 array or bf16 raw bits."""
     n = int(np.prod(shape)) if len(shape) else 1
     out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
     for s in range(0, n, chunk):
@@ -52,6 +52,47 @@ def normal(rng: np.random.Generator, shape, dtype: str, chunk: int = 1 << 26) ->
         v = rng.standard_normal(e - s, dtype=np.float32)
         out[s:e] = v if dtype == "f32" else bf16_bits(v)
     return out.reshape(shape)
+
+
+_CHUNK = 1 << 22  # values per independent sub-stream; fixed, so results do not depend on threads
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)))
+    return _POOL
+
+
+class Draws:
+    """The random source of one case.
+
+    Integers (lengths, permutations) come from one generator seeded by the
+    case seed.  Each value array gets its own child of the case's SeedSequence,
+    spawned in draw order, and is filled in fixed chunks of 2^22 values, chunk i
+    drawn from the i-th grandchild -- so large arrays fill in parallel threads
+    and the values depend only on (seed, draw order, shape)."""
+
+    def __init__(self, seed: int):
+        self.ss = np.random.SeedSequence(seed)
+        self.rng = np.random.default_rng(self.ss.spawn(1)[0])
+
+    def normal(self, shape, dtype: str) -> np.ndarray:
+        child = self.ss.spawn(1)[0]
+        n = int(np.prod(shape)) if len(shape) else 1
+        out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+        starts = list(range(0, n, _CHUNK))
+        seeds = child.spawn(len(starts))
+
+        def fill(i):
+            s = starts[i]
+            e = min(n, s + _CHUNK)
+            v = np.random.default_rng(seeds[i]).standard_normal(e - s, dtype=np.float32)
+            out[s:e] = v if dtype == "f32" else bf16_bits(v)
+
+        list(_pool().map(fill, range(len(starts))))
+        return out.reshape(shape)
 
 
 def nan_fill(a: np.ndarray) -> None:
@@ -166,7 +207,8 @@ def decode_case(seed: int, B: int, H: int, Hkv: int, D: int, dtype: str, *, bloc
                 scale: Optional[float] = None, table: Optional[np.ndarray] = None,
                 name: str = "decode") -> Case:
     """Decode case: one new token per sequence at position seq_lens[b] - 1."""
-    rng = np.random.default_rng(seed)
+    dr = Draws(seed)
+    rng = dr.rng
     if seq_lens is None:
         lo, hi = len_range
         seq_lens = rng.integers(lo, hi + 1, size=B)
@@ -178,18 +220,18 @@ def decode_case(seed: int, B: int, H: int, Hkv: int, D: int, dtype: str, *, bloc
     else:
         bt, nb = _tables(rng, B, seq_lens, block_size, max_blocks, B * max_blocks, spare_frac,
                          null_block, window)
-    q = normal(rng, (B, H, D), dtype)
-    q_rope = normal(rng, (B, H, rope_dim), dtype) if rope_dim else None
-    k_cache = normal(rng, (nb, block_size, Hkv, D), dtype)
-    v_cache = None if rope_dim else normal(rng, (nb, block_size, Hkv, D), dtype)
-    k_rope_cache = normal(rng, (nb, block_size, Hkv, rope_dim), dtype) if rope_dim else None
+    q = dr.normal((B, H, D), dtype)
+    q_rope = dr.normal((B, H, rope_dim), dtype) if rope_dim else None
+    k_cache = dr.normal((nb, block_size, Hkv, D), dtype)
+    v_cache = None if rope_dim else dr.normal((nb, block_size, Hkv, D), dtype)
+    k_rope_cache = dr.normal((nb, block_size, Hkv, rope_dim), dtype) if rope_dim else None
     if null_block:
         for a in (k_cache, v_cache, k_rope_cache):
             if a is not None:
                 nan_fill(a[0])
-    new_k = normal(rng, (B, Hkv, D), dtype)
-    new_v = None if rope_dim else normal(rng, (B, Hkv, D), dtype)
-    new_k_rope = normal(rng, (B, Hkv, rope_dim), dtype) if rope_dim else None
+    new_k = dr.normal((B, Hkv, D), dtype)
+    new_v = None if rope_dim else dr.normal((B, Hkv, D), dtype)
+    new_k_rope = dr.normal((B, Hkv, rope_dim), dtype) if rope_dim else None
     if scale is None:
         scale = 1.0 / math.sqrt(D + rope_dim)
     return Case(name=name, kind="decode", dtype=dtype, B=B, H=H, Hkv=Hkv, D=D, rope_dim=rope_dim,
@@ -206,7 +248,8 @@ def prefill_case(seed: int, B: int, H: int, Hkv: int, D: int, dtype: str, *, cac
                  rope_dim: int = 0, scale: Optional[float] = None, null_block: bool = False,
                  spare_frac: float = 0.1, name: str = "prefill") -> Case:
     """Chunked prefill: sequence b holds cached[b] tokens and gets new[b] more."""
-    rng = np.random.default_rng(seed)
+    dr = Draws(seed)
+    rng = dr.rng
     cached = np.broadcast_to(np.asarray(cached, dtype=np.int32), (B,)).copy()
     new = np.broadcast_to(np.asarray(new, dtype=np.int32), (B,)).copy()
     seq_lens = (cached + new).astype(np.int32)
@@ -215,18 +258,18 @@ def prefill_case(seed: int, B: int, H: int, Hkv: int, D: int, dtype: str, *, cac
     bt, nb = _tables(rng, B, seq_lens, block_size, max_blocks, B * max_blocks, spare_frac,
                      null_block, 0)
     T = int(new.sum())
-    q = normal(rng, (T, H, D), dtype)
-    q_rope = normal(rng, (T, H, rope_dim), dtype) if rope_dim else None
-    k_cache = normal(rng, (nb, block_size, Hkv, D), dtype)
-    v_cache = None if rope_dim else normal(rng, (nb, block_size, Hkv, D), dtype)
-    k_rope_cache = normal(rng, (nb, block_size, Hkv, rope_dim), dtype) if rope_dim else None
+    q = dr.normal((T, H, D), dtype)
+    q_rope = dr.normal((T, H, rope_dim), dtype) if rope_dim else None
+    k_cache = dr.normal((nb, block_size, Hkv, D), dtype)
+    v_cache = None if rope_dim else dr.normal((nb, block_size, Hkv, D), dtype)
+    k_rope_cache = dr.normal((nb, block_size, Hkv, rope_dim), dtype) if rope_dim else None
     if null_block:
         for a in (k_cache, v_cache, k_rope_cache):
             if a is not None:
                 nan_fill(a[0])
-    new_k = normal(rng, (T, Hkv, D), dtype)
-    new_v = None if rope_dim else normal(rng, (T, Hkv, D), dtype)
-    new_k_rope = normal(rng, (T, Hkv, rope_dim), dtype) if rope_dim else None
+    new_k = dr.normal((T, Hkv, D), dtype)
+    new_v = None if rope_dim else dr.normal((T, Hkv, D), dtype)
+    new_k_rope = dr.normal((T, Hkv, rope_dim), dtype) if rope_dim else None
     cu = np.zeros(B + 1, dtype=np.int32)
     cu[1:] = np.cumsum(new)
     bidx = np.repeat(np.arange(B, dtype=np.int32), new)
