@@ -42,7 +42,28 @@ def parse_args():
     ap.add_argument("--split-tokens", type=int, default=0, help="decode partition size (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the hot path, time a plain device copy of this many MiB (the reference "
+                         "for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(torch, mib, steps):
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
+                      "copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def _dev(torch, a):
@@ -78,6 +99,40 @@ def algorithmic_bytes(case):
     qo = q_rows * (case.D + case.rope_dim) * eb + q_rows * case.D * eb
     attn = kv + qo + int(blocks.sum()) * 4 + case.B * 4
     return resolve, write, attn, kv
+
+
+# Counter-measured HBM bytes per launch of the dominant kernel, kept in the profile
+# summary together with a hash of the kernel sources they were taken on.  When the
+# sources have changed since, the figure no longer describes the kernel: null.
+PROFILED = {
+    "mha_decode_7b": ("decode_valu_mha_decode_7b.md",
+                      ["paged_kv_cache_80_amd/csrc/decode.hip", "paged_kv_cache_80_amd/csrc/device_common.h"]),
+}
+
+
+def profiled_traffic(workload):
+    if workload not in PROFILED:
+        return None
+    name, sources = PROFILED[workload]
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    import hashlib
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if fields.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(case, target_s):
@@ -118,6 +173,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        copy_calibration(torch, args.copy_calibration_mib, args.steps)
+        return
     pkv.load()
 
     case = workloads.WORKLOADS[args.workload](args.seed)
@@ -195,7 +253,8 @@ def main():
         "tokens_per_s": round(case.new_pos.size / (ms_step * 1e-3), 1),
         "attention_ms": round(ms_attn, 4),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic(args.workload),
                      "kernel": "paged_attn_decode" if case.kind == "decode" else "paged_attn_prefill",
                      "bytes_per_launch": a_b},
     }
