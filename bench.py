@@ -135,6 +135,25 @@ def profiled_traffic(workload):
         return None
 
 
+def algorithmic_flops(case):
+    """Multiply-adds x 2 of the attention call: q.k over the logit width and p.v over the value
+    width, for every (query row, head, visible key)."""
+    L = case.seq_lens.astype(np.int64)
+    if case.kind == "decode":
+        lo = np.maximum(0, L - case.window) if case.window else np.zeros_like(L)
+        pairs = int((L - lo).sum()) * case.H
+    else:
+        cu = case.cu_seqlens_q
+        pairs = 0
+        for b in range(case.B):
+            n = int(cu[b + 1] - cu[b])
+            pos = L[b] - n + np.arange(n, dtype=np.int64)
+            vis = pos + 1 if not case.window else np.minimum(pos + 1, case.window)
+            pairs += int(vis.sum())
+        pairs *= case.H
+    return pairs * 2 * ((case.D + case.rope_dim) + case.D)
+
+
 def cpu_baseline(case, target_s):
     """The oracle, as it stands, on the host cores: whole steps of the same workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -230,9 +249,20 @@ def main():
     ms_attn = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
 
     r_b, w_b, a_b, kv_b = algorithmic_bytes(case)
+    flops = algorithmic_flops(case)
     step_bytes = r_b + w_b + a_b
     value = step_bytes / (ms_step * 1e-3) / 1e9
     attn_gbs = a_b / (ms_attn * 1e-3) / 1e9
+    attn_tflops = flops / (ms_attn * 1e-3) / 1e12
+    kernel = "paged_attn_decode" if case.kind == "decode" else "paged_attn_prefill"
+    if case.kind == "prefill":
+        roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+    roofline.update({"traffic": profiled_traffic(args.workload), "kernel": kernel, "bytes_per_launch": a_b,
+                     "flops_per_launch": flops})
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -252,11 +282,9 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(case.new_pos.size / (ms_step * 1e-3), 1),
         "attention_ms": round(ms_attn, 4),
-        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": profiled_traffic(args.workload),
-                     "kernel": "paged_attn_decode" if case.kind == "decode" else "paged_attn_prefill",
-                     "bytes_per_launch": a_b},
+        "attention_GBps": round(attn_gbs, 2),
+        "mfma_util": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

@@ -115,9 +115,18 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
   } else {
     // Enough workgroups to fill 256 CUs several times, partitions of at most a
     // few hundred KiB so ragged lengths balance.
-    const int64_t units = (int64_t)p->batch * c->num_kv_heads;
-    const int32_t part_tokens = units >= 1024 ? 2048 : 512;
-    bpp = std::max(1, part_tokens / bs);
+    int32_t part_tokens;
+    if (is_mla(c)) {
+      // One workgroup holds up to 128 heads; aim for about one workgroup per CU
+      // with partitions long enough that the partial outputs stay a small
+      // fraction of the latent bytes.
+      const int64_t units = (int64_t)p->batch * std::max(1, p->num_q_heads / 128);
+      part_tokens = units >= 256 ? 1 << 30 : units >= 128 ? 4096 : 2048;
+    } else {
+      const int64_t units = (int64_t)p->batch * c->num_kv_heads;
+      part_tokens = units >= 1024 ? 2048 : 512;
+    }
+    bpp = (int32_t)std::max<int64_t>(1, part_tokens / bs);
   }
   bpp = std::max(1, std::min({bpp, span, kMaxBpp}));
   DecodePlan plan;
@@ -215,11 +224,45 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (plan.ws_bytes > 0 && !aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (is_mla(cache)) return fail(PKV_ERR_UNSUPPORTED, "MLA decode is not built yet");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  float* ws_o = plan.max_np > 1 ? static_cast<float*>(workspace) : nullptr;
+  float* ws_ml =
+      plan.max_np > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset) : nullptr;
+  if (is_mla(cache)) {
+    if (!pkv::mla_decode_supported(cache->dtype, cache->head_dim, cache->rope_dim, params->num_q_heads))
+      return fail(PKV_ERR_UNSUPPORTED, "MLA decode: needs bf16, latent 512, rope 64 and H a multiple of 16");
+    pkv::MlaArgs m{};
+    m.q = q;
+    m.q_rope = q_rope;
+    m.c_nope = cache->k_cache;
+    m.c_rope = cache->k_rope_cache;
+    m.block_table = block_table;
+    m.seq_lens = seq_lens;
+    m.out = out;
+    m.ws_o = ws_o;
+    m.ws_ml = ws_ml;
+    m.batch = params->batch;
+    m.num_q_heads = params->num_q_heads;
+    m.max_blocks_per_seq = params->max_blocks_per_seq;
+    m.block_size_log2 = log2i(cache->block_size);
+    m.blocks_per_part = plan.bpp;
+    m.max_np = plan.max_np;
+    m.window = params->window;
+    m.scale_log2e = params->scale * pkv::kLog2e;
+    m.out_dtype = params->out_dtype;
+    hipError_t e = pkv::launch_mla_decode(m, st);
+    if (e != hipSuccess) return from_hip(e, "MLA decode launch");
+    if (plan.max_np > 1) {
+      e = pkv::launch_decode_combine(ws_o, ws_ml, seq_lens, params->batch, params->num_q_heads, cache->head_dim,
+                                     plan.max_np, m.block_size_log2, plan.bpp, params->window, out,
+                                     params->out_dtype, st);
+      if (e != hipSuccess) return from_hip(e, "decode combine launch");
+    }
+    return ok();
+  }
   if (!pkv::decode_valu_supported(cache->dtype, cache->head_dim, group))
     return fail(PKV_ERR_UNSUPPORTED, "decode: dtype %d, head_dim %d, group %d not supported", cache->dtype,
                 cache->head_dim, group);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
   pkv::DecodeArgs a{};
   a.q = q;
   a.k_cache = cache->k_cache;
@@ -227,8 +270,8 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.out = out;
-  a.ws_o = plan.max_np > 1 ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = plan.max_np > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset) : nullptr;
+  a.ws_o = ws_o;
+  a.ws_ml = ws_ml;
   a.batch = params->batch;
   a.num_q_heads = params->num_q_heads;
   a.num_kv_heads = cache->num_kv_heads;
@@ -256,20 +299,50 @@ size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_pag
   (void)params;
   (void)cache;
   (void)total_q;
-  return 0;
+  return 0;  // every prefill workgroup walks all keys of its rows: no partials
 }
 
 pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged_cache* cache,
                               const int32_t* block_table, const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,
                               int32_t total_q, int32_t max_q_len, const pkv_attn_params* params, void* out,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  (void)q, (void)q_rope, (void)block_table, (void)cu_seqlens_q, (void)seq_lens_kv, (void)total_q,
-      (void)max_q_len, (void)out, (void)workspace, (void)workspace_bytes, (void)stream;
+  (void)workspace;
+  (void)workspace_bytes;
   pkv_status s = check_cache(cache);
   if (s) return s;
   s = check_params(params, cache);
   if (s) return s;
-  return fail(PKV_ERR_UNSUPPORTED, "prefill is not built yet");
+  if (total_q < 0 || max_q_len < 0) return fail(PKV_ERR_INVALID_ARG, "total_q and max_q_len must be >= 0");
+  if (params->split_tokens != 0) return fail(PKV_ERR_INVALID_ARG, "split_tokens applies to decode only");
+  if (params->batch == 0 || total_q == 0) return ok();
+  if (!q || !block_table || !cu_seqlens_q || !seq_lens_kv || !out)
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((q_rope != nullptr) != is_mla(cache))
+    return fail(PKV_ERR_INVALID_ARG, "q_rope and k_rope must be given together or not at all");
+  if (!aligned16(q) || !aligned16(out)) return fail(PKV_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+  if (is_mla(cache)) return fail(PKV_ERR_UNSUPPORTED, "MLA prefill is not implemented");
+  if (!pkv::prefill_mfma_supported(cache->dtype, cache->head_dim))
+    return fail(PKV_ERR_UNSUPPORTED, "prefill: needs bf16 and head_dim 64 or 128 (got dtype %d, head_dim %d)",
+                cache->dtype, cache->head_dim);
+  pkv::PrefillArgs a{};
+  a.q = q;
+  a.k_cache = cache->k_cache;
+  a.v_cache = cache->v_cache;
+  a.block_table = block_table;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seq_lens_kv = seq_lens_kv;
+  a.out = out;
+  a.batch = params->batch;
+  a.num_q_heads = params->num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.max_blocks_per_seq = params->max_blocks_per_seq;
+  a.block_size_log2 = log2i(cache->block_size);
+  a.max_q_len = max_q_len;
+  a.window = params->window;
+  a.scale_log2e = params->scale * pkv::kLog2e;
+  a.out_dtype = params->out_dtype;
+  return from_hip(pkv::launch_prefill_mfma(a, static_cast<hipStream_t>(stream)), "prefill launch");
 }
 
 }  // extern "C"

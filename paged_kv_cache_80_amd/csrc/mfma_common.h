@@ -1,0 +1,98 @@
+// mfma_common.h -- helpers for the bf16 matrix-core (MFMA) attention kernels.
+//
+// v_mfma_f32_16x16x32_bf16 computes D[16x16] += A[16x32] * B[32x16] per wave.
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each as 8 bf16
+// covering the contraction slots of lane group l / 16; the same slot function is
+// used for A and B, so any consistent assignment of contraction indices to
+// (lane group, element) pairs computes the same sum.  D comes back as 4 floats
+// per lane: D[4*(l/16) + r][l % 16], r = 0..3.
+//
+// Both attention products are taken in transposed form so that a lane's query
+// column never changes:
+//     S^T[key, col] = sum_d K[key, d] * Q[col, d]        (A = K tile, B = Q^T)
+//     O^T[d, col]  += sum_key V^T[d, key] * P^T[key, col] (A = V^T tile, B = P^T)
+// S^T's accumulator layout (lane holds column l%16, keys 4*(l/16)+r of a 16-key
+// sub-tile) is exactly the B-operand layout P^T needs for a 32-key step when the
+// contraction slot e of lane group g means key 4g+e (e < 4) or 16+4g+(e-4) (e >= 4).
+#pragma once
+
+#include "device_common.h"
+#include "pkv.h"
+
+namespace pkv {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t f32x4_zero() {
+  f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// Probabilities in [0, 1] split as p = hi + lo + r with hi, lo bf16 (both taken
+// by truncation, |r| < 2^-15 p), so two bf16 products carry p to ~16 bits: the
+// P.V product keeps fp32-class accuracy instead of bf16's 2^-9.
+__device__ __forceinline__ void split_bf16(float p, uint32_t& hi, uint32_t& lo) {
+  const uint32_t u = __float_as_uint(p);
+  hi = u & 0xffff0000u;
+  const float r = p - __uint_as_float(hi);  // exact
+  lo = __float_as_uint(r) & 0xffff0000u;
+}
+
+// Pack 8 probabilities (slot order) into hi and lo bf16x8 operands.
+__device__ __forceinline__ void pack_p(const float* p8, uint4& hi, uint4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) split_bf16(p8[e], h[e], l[e]);
+  hi.x = (h[0] >> 16) | h[1];
+  hi.y = (h[2] >> 16) | h[3];
+  hi.z = (h[4] >> 16) | h[5];
+  hi.w = (h[6] >> 16) | h[7];
+  lo.x = (l[0] >> 16) | l[1];
+  lo.y = (l[2] >> 16) | l[3];
+  lo.z = (l[4] >> 16) | l[5];
+  lo.w = (l[6] >> 16) | l[7];
+}
+
+// Two bf16 of two keys at one dimension, low half = first key.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+
+// Interleave 8 bf16 of key k0 (a) and key k1 (b) into 8 dwords, one per dimension.
+__device__ __forceinline__ void interleave_pairs(const uint4& a, const uint4& b, uint32_t* w) {
+  w[0] = pair_lo(a.x, b.x);
+  w[1] = pair_hi(a.x, b.x);
+  w[2] = pair_lo(a.y, b.y);
+  w[3] = pair_hi(a.y, b.y);
+  w[4] = pair_lo(a.z, b.z);
+  w[5] = pair_hi(a.z, b.z);
+  w[6] = pair_lo(a.w, b.w);
+  w[7] = pair_hi(a.w, b.w);
+}
+
+__device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+
+// Store 4 consecutive output elements of one row.
+__device__ __forceinline__ void store4(void* out, int64_t idx, const float* v, int32_t out_dtype) {
+  if (out_dtype == PKV_BF16) {
+    uint2 w;
+    w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = w;
+  } else {
+    uint4 w;
+    w.x = __float_as_uint(v[0]);
+    w.y = __float_as_uint(v[1]);
+    w.z = __float_as_uint(v[2]);
+    w.w = __float_as_uint(v[3]);
+    *reinterpret_cast<uint4*>(static_cast<float*>(out) + idx) = w;
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,217 @@
+// mla.hip -- MLA absorbed-form decode over a paged latent cache on bf16 MFMA.
+//
+// The cache holds, per token, the compressed latent c (kv_lora_rank = 512) and
+// a separate rotary part c_r (64).  With the projections absorbed, every query
+// head h scores a key as q_nope[h].c + q_rope[h].c_r and the value is c itself
+// ("KVCache optimisation skill", mode 3: key = value = cache_nope, rope passed
+// separately; "KV Cache notes", MLA section: one latent shared by all heads).
+// So all H query heads read the same 1152-byte row per token: Q-tile x key-tile
+// is a dense contraction (H x 576 by 576 x keys, then H x keys by keys x 512).
+//
+// Work split.  One workgroup per (sequence, key partition, group of up to 128
+// heads); each wave owns 16 heads and keeps their q (576 bf16) in registers and
+// their O^T (512 x 16 fp32) in accumulators.  32-key tiles of the latent are
+// staged in LDS twice: row-major [key][latent | rope] for S^T = C.Q^T and
+// transposed [dim][key] for O^T += C^T.P^T.  Partials (m, l, o) of each
+// partition go to the workspace and the split-K combine of decode.hip merges
+// them, exactly as for standard decode.
+#include "mfma_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kD = 512;        // latent width (value width)
+constexpr int kR = 64;         // rope width
+constexpr int kK = kD + kR;    // logit contraction width
+constexpr int kKeyTile = 32;
+constexpr int kCPad = 8;
+constexpr int kVPad = 4;
+
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void mla_decode_kernel(MlaArgs a) {
+  constexpr int KS = kK / 32;   // 18 contraction steps (16 latent + 2 rope)
+  constexpr int DT = kD / 16;   // 32 row tiles of O^T
+  constexpr int NT = NW * kWave;
+  __shared__ __attribute__((aligned(16))) uint16_t c_lds[kKeyTile][kK + kCPad];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kD][kKeyTile + kVPad];
+
+  const int part = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int H = a.num_q_heads;
+  const int head = (hg * NW + wave) * 16 + l16;
+  const int64_t qrow = (int64_t)b * H + head;
+
+  const int32_t L = a.seq_lens[b];
+  const KeySpan sp = decode_span(L, a.window, a.block_size_log2, a.blocks_per_part);
+  if (part >= sp.np) {
+    if (a.max_np == 1 && sp.np == 0 && part == 0) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int dt = 0; dt < DT; ++dt) store4(a.out, qrow * kD + 16 * dt + 4 * lg, z, a.out_dtype);
+    }
+    return;
+  }
+  const int bs_log2 = a.block_size_log2;
+  const int bs_mask = (1 << bs_log2) - 1;
+  const int blk0 = sp.first_blk + part * a.blocks_per_part;
+  const int nblk = min(a.blocks_per_part, ((L - 1) >> bs_log2) - blk0 + 1);
+  const int tok_begin = max(sp.lo, blk0 << bs_log2);
+  const int tok_end = min(L, (blk0 + nblk) << bs_log2);
+
+  const uint16_t* qn = static_cast<const uint16_t*>(a.q);
+  const uint16_t* qr = static_cast<const uint16_t*>(a.q_rope);
+  uint4 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = ks < kD / 32 ? ld16(qn + qrow * kD + 32 * ks + 8 * lg)
+                          : ld16(qr + qrow * kR + 32 * (ks - kD / 32) + 8 * lg);
+
+  f32x4_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_zero();
+  float m = kNegInf, l = 0.f;
+
+  const uint16_t* cn = static_cast<const uint16_t*>(a.c_nope);
+  const uint16_t* cr = static_cast<const uint16_t*>(a.c_rope);
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq;
+
+  for (int t0 = tok_begin & ~(kKeyTile - 1); t0 < tok_end; t0 += kKeyTile) {
+    __syncthreads();
+    // Latent rows: a lane takes one 16-byte chunk of two neighbouring keys and
+    // writes it row-major and, interleaved per dimension, transposed.
+    for (int idx = tid; idx < (kKeyTile / 2) * (kD / 8); idx += NT) {
+      const int pr = idx % (kKeyTile / 2);
+      const int c = idx / (kKeyTile / 2);
+      const int j = t0 + 2 * pr;
+      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
+      if (j >= tok_begin && j < tok_end) {
+        const int64_t slot = ((int64_t)bt[j >> bs_log2] << bs_log2) + (j & bs_mask);
+        v0 = ld16(cn + slot * kD + 8 * c);
+      }
+      if (j + 1 >= tok_begin && j + 1 < tok_end) {
+        const int64_t slot = ((int64_t)bt[(j + 1) >> bs_log2] << bs_log2) + ((j + 1) & bs_mask);
+        v1 = ld16(cn + slot * kD + 8 * c);
+      }
+      *reinterpret_cast<uint4*>(&c_lds[2 * pr][8 * c]) = v0;
+      *reinterpret_cast<uint4*>(&c_lds[2 * pr + 1][8 * c]) = v1;
+      uint32_t w[8];
+      interleave_pairs(v0, v1, w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(&vt_lds[8 * c + e][2 * pr]) = w[e];
+    }
+    // Rope rows beside the latent in the row-major tile.
+    for (int idx = tid; idx < kKeyTile * (kR / 8); idx += NT) {
+      const int r = idx / (kR / 8);
+      const int c = idx - r * (kR / 8);
+      const int j = t0 + r;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j >= tok_begin && j < tok_end) {
+        const int64_t slot = ((int64_t)bt[j >> bs_log2] << bs_log2) + (j & bs_mask);
+        v = ld16(cr + slot * kR + 8 * c);
+      }
+      *reinterpret_cast<uint4*>(&c_lds[r][kD + 8 * c]) = v;
+    }
+    __syncthreads();
+
+    f32x4_t s[kKeyTile / 16];
+#pragma unroll
+    for (int u = 0; u < kKeyTile / 16; ++u) {
+      s[u] = f32x4_zero();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[u] = mfma_bf16(lds16(&c_lds[16 * u + l16][32 * ks + 8 * lg]), qf[ks], s[u]);
+    }
+    float mt = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kKeyTile / 16; ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = t0 + 16 * u + 4 * lg + r;
+        const float x = (j >= tok_begin && j < tok_end) ? s[u][r] * a.scale_log2e : kNegInf;
+        s[u][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float alpha = rescale(m, mn);
+    const float msub = mn == kNegInf ? 0.f : mn;
+    float p8[8];
+    float ls = 0.f;
+#pragma unroll
+    for (int u = 0; u < kKeyTile / 16; ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = exp2_fast(s[u][r] - msub);
+        p8[4 * u + r] = p;
+        ls += p;
+      }
+    }
+    l = l * alpha + ls;
+    m = mn;
+    uint4 phi, plo;
+    pack_p(p8, phi, plo);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint2 x0 = lds8(&vt_lds[16 * dt + l16][4 * lg]);
+      const uint2 x1 = lds8(&vt_lds[16 * dt + l16][16 + 4 * lg]);
+      const uint4 af = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      o[dt] *= alpha;
+      o[dt] = mfma_bf16(af, phi, o[dt]);
+      o[dt] = mfma_bf16(af, plo, o[dt]);
+    }
+  }
+
+  float lsum = l;
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (a.max_np == 1) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const float v[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
+      store4(a.out, qrow * kD + 16 * dt + 4 * lg, v, a.out_dtype);
+    }
+  } else {
+    float* wo = a.ws_o + (qrow * a.max_np + part) * kD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const float v[4] = {o[dt][0], o[dt][1], o[dt][2], o[dt][3]};
+      store4(wo, 16 * dt + 4 * lg, v, PKV_F32);
+    }
+    if (lg == 0) {
+      a.ws_ml[(qrow * a.max_np + part) * 2 + 0] = m;
+      a.ws_ml[(qrow * a.max_np + part) * 2 + 1] = lsum;
+    }
+  }
+}
+
+}  // namespace
+
+bool mla_decode_supported(int32_t dtype, int32_t head_dim, int32_t rope_dim, int32_t num_q_heads) {
+  return dtype == PKV_BF16 && head_dim == kD && rope_dim == kR && num_q_heads % 16 == 0;
+}
+
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
+  const int tiles16 = a.num_q_heads / 16;
+  if (a.batch == 0) return hipSuccess;
+  // Up to 8 waves (128 heads) per workgroup; the head groups tile H exactly.
+  int nw = 8;
+  while (tiles16 % nw) nw >>= 1;
+  const dim3 grid(a.max_np, tiles16 / nw, a.batch);
+  switch (nw) {
+    case 8: mla_decode_kernel<8><<<grid, 8 * kWave, 0, stream>>>(a); break;
+    case 4: mla_decode_kernel<4><<<grid, 4 * kWave, 0, stream>>>(a); break;
+    case 2: mla_decode_kernel<2><<<grid, 2 * kWave, 0, stream>>>(a); break;
+    default: mla_decode_kernel<1><<<grid, 1 * kWave, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -50,4 +50,40 @@ hipError_t launch_decode_combine(const float* ws_o, const float* ws_ml, const in
                                  int32_t block_size_log2, int32_t blocks_per_part, int32_t window,
                                  void* out, int32_t out_dtype, hipStream_t stream);
 
+// Chunked causal prefill on MFMA (prefill.hip).
+struct PrefillArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  const int32_t* cu_seqlens_q;
+  const int32_t* seq_lens_kv;
+  void* out;
+  int32_t batch, num_q_heads, num_kv_heads, head_dim;
+  int32_t max_blocks_per_seq, block_size_log2, max_q_len, window;
+  float scale_log2e;
+  int32_t out_dtype;
+};
+hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+bool prefill_mfma_supported(int32_t dtype, int32_t head_dim);
+
+// MLA absorbed decode on MFMA (mla.hip); partials share the decode workspace layout.
+struct MlaArgs {
+  const void* q;       // [B, H, 512]
+  const void* q_rope;  // [B, H, 64]
+  const void* c_nope;  // [num_blocks, bs, 1, 512]
+  const void* c_rope;  // [num_blocks, bs, 1, 64]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;
+  float* ws_o;
+  float* ws_ml;
+  int32_t batch, num_q_heads;
+  int32_t max_blocks_per_seq, block_size_log2, blocks_per_part, max_np, window;
+  float scale_log2e;
+  int32_t out_dtype;
+};
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
+bool mla_decode_supported(int32_t dtype, int32_t head_dim, int32_t rope_dim, int32_t num_q_heads);
+
 }  // namespace pkv

@@ -1,0 +1,161 @@
+"""GPU parity of the MFMA kernels through the C ABI: chunked causal prefill and MLA absorbed
+decode, against the CPU oracle.
+
+Bars as in test_gpu_decode.py: per output row ||out - bf16(oracle)|| / ||bf16(oracle)|| <= 2e-3
+for bf16 outputs, and <= 1e-4 against the unrounded oracle in fp32-output mode (the
+probabilities enter P.V as a hi + lo bf16 pair, so only fp32 accumulation error remains).
+"""
+import numpy as np
+import pytest
+
+import workloads
+from helpers import oracle_run
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-3
+ACC_TOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_80_amd as pkv
+    pkv.load()
+
+
+from gpu_util import DeviceCase, as_f64, assert_rows_close, host  # noqa: E402
+
+
+# --------------------------------------------------------------------------- prefill
+
+PREFILL_MATRIX = [
+    # B, H, Hkv, D, bs, cached, new, window
+    (2, 4, 4, 128, 128, [5, 0], [7, 70], 0),
+    (3, 8, 2, 128, 16, [9, 1, 130], [3, 64, 77], 0),
+    (4, 32, 8, 128, 128, [300, 0, 64, 1000], [200, 33, 1, 128], 0),
+    (2, 12, 4, 64, 32, [40, 100], [90, 5], 0),        # G = 3
+    (3, 8, 1, 128, 64, [0, 500, 17], [150, 0, 99], 0),  # MQA, an empty sequence
+    (2, 16, 4, 128, 128, [600, 90], [130, 200], 100),  # sliding window
+    (2, 8, 8, 64, 16, [70, 3], [40, 60], 17),
+]
+
+
+@pytest.mark.parametrize("shape", PREFILL_MATRIX)
+def test_prefill_matches_oracle(orc, shape):
+    B, H, Hkv, D, bs, cached, new, w = shape
+    case = workloads.prefill_case(sum(cached) + w, B, H, Hkv, D, "bf16", cached=cached, new=new,
+                                  block_size=bs, window=w, null_block=True)
+    ref, c_ref, slots_ref = oracle_run(orc, case)
+    d = DeviceCase(case)
+    out, slots = d.run()
+    np.testing.assert_array_equal(host(slots), slots_ref)
+    assert host(d.cache.k_cache).tobytes() == c_ref.k_cache.tobytes()
+    assert_rows_close(out, ref, BF16_TOL)
+
+
+def test_prefill_fp32_accumulation(orc):
+    case = workloads.prefill_case(7, 3, 16, 4, 128, "bf16", cached=[700, 0, 260], new=[100, 300, 64],
+                                  block_size=64, null_block=True)
+    ref, _, _ = oracle_run(orc, case)
+    out, _ = DeviceCase(case).run(out_dtype=torch.float32)
+    assert_rows_close(out, ref, ACC_TOL)
+
+
+def test_prefill_single_row_equals_decode(orc):
+    """One new row per sequence through prefill is a decode step (q_len = 1)."""
+    lens = np.array([1, 77, 300, 129], dtype=np.int32)
+    dec = workloads.decode_case(8, 4, 8, 2, 128, "bf16", block_size=32, max_blocks=10, seq_lens=lens,
+                                null_block=True)
+    import paged_kv_cache_80_amd as pkv
+    d = DeviceCase(dec)
+    out_dec, _ = d.run(out_dtype=torch.float32)
+    cu = torch.arange(5, dtype=torch.int32, device="cuda")
+    out_pf = pkv.paged_attn_prefill(d.q.view(4, 8, 128), d.cache, d.block_table, cu, d.seq_lens, 1,
+                                    dec.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle_run(orc, dec)
+    assert_rows_close(out_pf, ref, ACC_TOL)
+    assert_rows_close(out_dec, ref, ACC_TOL)
+
+
+def test_prefill_full_size_sampled(orc):
+    """B=8, H=32/8, d=128: 4096 cached + 512 new rows per sequence (sampled rows)."""
+    case = workloads.chunked_prefill(0)
+    d = DeviceCase(case)
+    out, slots = d.run()
+    rng = np.random.default_rng(0)
+    T = case.q.shape[0]
+    units = np.unique(np.concatenate([rng.choice(T * case.H, 256, replace=False),
+                                      np.arange(case.H), (T - 1) * case.H + np.arange(case.H)]))
+    ref, _, slots_ref = oracle_run(orc, case, units=units, inplace=True)
+    np.testing.assert_array_equal(host(slots), slots_ref)
+    assert np.all(np.isfinite(as_f64(out)))
+    assert_rows_close(out, ref, BF16_TOL, rows=units)
+
+
+# --------------------------------------------------------------------------- MLA absorbed decode
+
+MLA_MATRIX = [
+    # B, H, bs, max_blocks, len_range, window, split
+    (3, 16, 128, 4, (1, 512), 0, 0),
+    (4, 128, 64, 8, (1, 512), 0, 0),
+    (5, 32, 16, 40, (1, 640), 0, 64),
+    (2, 64, 128, 6, (600, 768), 0, 128),
+    (3, 128, 32, 20, (1, 640), 100, 0),
+    (6, 48, 128, 3, (1, 384), 0, 0),     # 3 head tiles -> one-wave groups
+]
+
+
+@pytest.mark.parametrize("shape", MLA_MATRIX)
+def test_mla_decode_matches_oracle(orc, shape):
+    B, H, bs, mb, lr, w, split = shape
+    case = workloads.decode_case(B * 7 + H, B, H, 1, 512, "bf16", block_size=bs, max_blocks=mb,
+                                 len_range=lr, window=w, null_block=True, rope_dim=64,
+                                 scale=1.0 / np.sqrt(576.0))
+    ref, c_ref, slots_ref = oracle_run(orc, case)
+    d = DeviceCase(case)
+    out, slots = d.run(split_tokens=split)
+    np.testing.assert_array_equal(host(slots), slots_ref)
+    assert host(d.cache.k_rope_cache).tobytes() == c_ref.k_rope_cache.tobytes()
+    assert_rows_close(out, ref, BF16_TOL)
+
+
+@pytest.mark.parametrize("split", [0, 32, 128])
+def test_mla_fp32_accumulation(orc, split):
+    case = workloads.decode_case(9, 4, 32, 1, 512, "bf16", block_size=32, max_blocks=24,
+                                 len_range=(1, 768), null_block=True, rope_dim=64)
+    ref, _, _ = oracle_run(orc, case)
+    out, _ = DeviceCase(case).run(out_dtype=torch.float32, split_tokens=split)
+    assert_rows_close(out, ref, ACC_TOL)
+
+
+def test_mla_empty_and_single_key(orc):
+    lens = np.array([0, 1, 0, 2], dtype=np.int32)
+    case = workloads.decode_case(10, 4, 16, 1, 512, "bf16", block_size=16, max_blocks=2, seq_lens=lens,
+                                 null_block=True, rope_dim=64)
+    ref, c_ref, slots = oracle_run(orc, case)
+    for split in (0, 16):
+        out, _ = DeviceCase(case).run(split_tokens=split)
+        o = host(out)
+        assert np.all(o[0] == 0) and np.all(o[2] == 0)
+        latent = c_ref.k_cache.reshape(-1, 512)[slots[1]]
+        assert all(o[1, h].tobytes() == latent.tobytes() for h in range(16))
+        assert_rows_close(out, ref, BF16_TOL)
+
+
+def test_mla_full_size_sampled(orc):
+    """B=64, 128 heads, latent 512 + rope 64, L=8192, shuffled 4096-block table (sampled rows)."""
+    case = workloads.mla_decode(0)
+    d = DeviceCase(case)
+    out, slots = d.run()
+    rng = np.random.default_rng(1)
+    units = np.unique(np.concatenate([rng.choice(case.B * case.H, 192, replace=False),
+                                      np.arange(case.H)]))
+    ref, c_ref, slots_ref = oracle_run(orc, case, units=units, inplace=True)
+    np.testing.assert_array_equal(host(slots), slots_ref)
+    assert np.all(np.isfinite(as_f64(out)))
+    assert_rows_close(out, ref, BF16_TOL, rows=units)
