@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "device_common.h"
@@ -104,6 +105,17 @@ struct DecodePlan {
 };
 
 constexpr int32_t kMaxBpp = 1024;
+
+// Tuning override for the MLA kernel's waves per workgroup (PKV_MLA_WAVES = 1, 2,
+// 4 or 8; unset = the library's choice).  Read once per process.
+int32_t mla_waves_override() {
+  static const int32_t v = [] {
+    const char* e = std::getenv("PKV_MLA_WAVES");
+    const int x = e ? std::atoi(e) : 0;
+    return (x == 1 || x == 2 || x == 4 || x == 8) ? x : 0;
+  }();
+  return v;
+}
 
 DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
   const int32_t bs = c->block_size;
@@ -250,6 +262,7 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
     m.window = params->window;
     m.scale_log2e = params->scale * pkv::kLog2e;
     m.out_dtype = params->out_dtype;
+    m.waves_per_group = mla_waves_override();
     hipError_t e = pkv::launch_mla_decode(m, st);
     if (e != hipSuccess) return from_hip(e, "MLA decode launch");
     if (plan.max_np > 1) {

@@ -75,6 +75,49 @@ __device__ __forceinline__ void interleave_pairs(const uint4& a, const uint4& b,
   w[7] = pair_hi(a.w, b.w);
 }
 
+// p0, p1 -> one dword holding bf16 truncations of both (p0 in the low half):
+// v_perm_b32 picks bytes 2,3 of p0 and bytes 2,3 of p1.
+__device__ __forceinline__ uint32_t pack_hi16(float p0, float p1) {
+  return __builtin_amdgcn_perm(__float_as_uint(p1), __float_as_uint(p0), 0x07060302u);
+}
+
+// Split 8 probabilities (slot order) into hi and lo bf16x8 operands with
+// p = hi + lo + r, |r| < 2^-15 p (hi and lo both truncated; p - hi is exact).
+__device__ __forceinline__ void pack_p_split(const float* p8, uint4& hi, uint4& lo) {
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = p8[e] - __uint_as_float(__float_as_uint(p8[e]) & 0xffff0000u);
+  hi.x = pack_hi16(p8[0], p8[1]);
+  hi.y = pack_hi16(p8[2], p8[3]);
+  hi.z = pack_hi16(p8[4], p8[5]);
+  hi.w = pack_hi16(p8[6], p8[7]);
+  lo.x = pack_hi16(r[0], r[1]);
+  lo.y = pack_hi16(r[2], r[3]);
+  lo.z = pack_hi16(r[4], r[5]);
+  lo.w = pack_hi16(r[6], r[7]);
+}
+
+// ---- gfx950 LDS paths -------------------------------------------------------
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16*l (lds_base must be the same for the whole wave).  The copy is
+// asynchronous and counted by vmcnt.
+__device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives 16-bit element (i % 4) of the 8-byte reads of lanes
+// 4k + i/4, k = 0..3.  If lane j of a group addresses row R0 + j/4 at column
+// C0 + 4*(j%4) of a row-major tile, lane i gets tile[R0 + k][C0 + i], k = 0..3:
+// a column of four rows, i.e. the MFMA operand of the transposed tile.
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  const bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 __device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 

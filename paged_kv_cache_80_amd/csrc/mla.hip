@@ -11,10 +11,13 @@
 // Work split.  One workgroup per (sequence, key partition, group of up to 128
 // heads); each wave owns 16 heads and keeps their q (576 bf16) in registers and
 // their O^T (512 x 16 fp32) in accumulators.  32-key tiles of the latent are
-// staged in LDS twice: row-major [key][latent | rope] for S^T = C.Q^T and
-// transposed [dim][key] for O^T += C^T.P^T.  Partials (m, l, o) of each
-// partition go to the workspace and the split-K combine of decode.hip merges
-// them, exactly as for standard decode.
+// copied straight into LDS with global_load_lds, double-buffered, one row per
+// wave instruction (rows padded so fragment reads spread over the banks); the
+// rope rows sit in a second, chunk-swizzled tile.  The same row-major latent
+// tile feeds S^T = C.Q^T (ds_read_b128) and, through ds_read_b64_tr_b16, the
+// transposed operand of O^T += C^T.P^T -- no second copy.  Partials (m, l, o)
+// of each partition go to the workspace and the split-K combine of decode.hip
+// merges them, exactly as for standard decode.
 #include "mfma_common.h"
 #include "pkv_internal.h"
 
@@ -23,18 +26,22 @@ namespace {
 
 constexpr int kD = 512;        // latent width (value width)
 constexpr int kR = 64;         // rope width
-constexpr int kK = kD + kR;    // logit contraction width
 constexpr int kKeyTile = 32;
-constexpr int kCPad = 8;
-constexpr int kVPad = 4;
+constexpr int kRowPad = 8;     // bf16 padding per latent row in LDS
+constexpr int kRow = kD + kRowPad;
+constexpr int kMaxBpp = 1024;  // table blocks per partition held in LDS
+
+__device__ __forceinline__ int rope_swz(int r) { return r & 7; }
 
 template <int NW>
-__global__ __launch_bounds__(NW * kWave) void mla_decode_kernel(MlaArgs a) {
-  constexpr int KS = kK / 32;   // 18 contraction steps (16 latent + 2 rope)
-  constexpr int DT = kD / 16;   // 32 row tiles of O^T
+__global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs a) {
+  constexpr int KS = (kD + kR) / 32;  // 18 contraction steps (16 latent + 2 rope)
+  constexpr int DT = kD / 16;         // 32 row tiles of O^T
   constexpr int NT = NW * kWave;
-  __shared__ __attribute__((aligned(16))) uint16_t c_lds[kKeyTile][kK + kCPad];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kD][kKeyTile + kVPad];
+  constexpr int kLoads = kKeyTile + kKeyTile * kR / (8 * kWave);  // 32 latent + 4 rope wave loads
+  __shared__ __attribute__((aligned(16))) uint16_t c_lds[2][kKeyTile][kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t r_lds[2][kKeyTile][kR];
+  __shared__ int32_t s_blk[kMaxBpp];
 
   const int part = blockIdx.x;
   const int hg = blockIdx.y;
@@ -63,6 +70,8 @@ __global__ __launch_bounds__(NW * kWave) void mla_decode_kernel(MlaArgs a) {
   const int nblk = min(a.blocks_per_part, ((L - 1) >> bs_log2) - blk0 + 1);
   const int tok_begin = max(sp.lo, blk0 << bs_log2);
   const int tok_end = min(L, (blk0 + nblk) << bs_log2);
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + blk0;
+  for (int i = tid; i < nblk; i += NT) s_blk[i] = bt[i];
 
   const uint16_t* qn = static_cast<const uint16_t*>(a.q);
   const uint16_t* qr = static_cast<const uint16_t*>(a.q_rope);
@@ -71,68 +80,64 @@ __global__ __launch_bounds__(NW * kWave) void mla_decode_kernel(MlaArgs a) {
   for (int ks = 0; ks < KS; ++ks)
     qf[ks] = ks < kD / 32 ? ld16(qn + qrow * kD + 32 * ks + 8 * lg)
                           : ld16(qr + qrow * kR + 32 * (ks - kD / 32) + 8 * lg);
+  __syncthreads();  // s_blk ready
+
+  const uint16_t* cn = static_cast<const uint16_t*>(a.c_nope);
+  const uint16_t* cr = static_cast<const uint16_t*>(a.c_rope);
+
+  // Keys outside [tok_begin, tok_end) re-read a visible row (masked later).
+  auto slot_of = [&](int j) -> int64_t {
+    j = min(max(j, tok_begin), tok_end - 1);
+    return ((int64_t)s_blk[(j >> bs_log2) - blk0] << bs_log2) + (j & bs_mask);
+  };
+  auto issue_tile = [&](int t0, int buf) {
+    for (int i = wave; i < kLoads; i += NW) {
+      if (i < kKeyTile) {  // one latent row per wave instruction: lane = 16-byte chunk
+        load_lds16(cn + slot_of(t0 + i) * kD + 8 * lane, &c_lds[buf][i][0]);
+      } else {             // eight rope rows per wave instruction
+        const int row0 = (i - kKeyTile) * 8;
+        const int r = row0 + (lane >> 3);
+        load_lds16(cr + slot_of(t0 + r) * kR + 8 * ((lane & 7) ^ rope_swz(r)), &r_lds[buf][row0][0]);
+      }
+    }
+  };
 
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_zero();
   float m = kNegInf, l = 0.f;
+  const float c2 = a.scale_log2e;
+  const int q4 = l16 & 3;
+  const int ra = 4 * lg + (l16 >> 2);  // rows of this lane's transposed reads
+  const int rb = ra + 16;
 
-  const uint16_t* cn = static_cast<const uint16_t*>(a.c_nope);
-  const uint16_t* cr = static_cast<const uint16_t*>(a.c_rope);
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq;
-
-  for (int t0 = tok_begin & ~(kKeyTile - 1); t0 < tok_end; t0 += kKeyTile) {
+  const int t_first = tok_begin & ~(kKeyTile - 1);
+  issue_tile(t_first, 0);
+  for (int t0 = t_first; t0 < tok_end; t0 += kKeyTile) {
+    const int buf = ((t0 - t_first) / kKeyTile) & 1;
+    wait_vmem();
     __syncthreads();
-    // Latent rows: a lane takes one 16-byte chunk of two neighbouring keys and
-    // writes it row-major and, interleaved per dimension, transposed.
-    for (int idx = tid; idx < (kKeyTile / 2) * (kD / 8); idx += NT) {
-      const int pr = idx % (kKeyTile / 2);
-      const int c = idx / (kKeyTile / 2);
-      const int j = t0 + 2 * pr;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (j >= tok_begin && j < tok_end) {
-        const int64_t slot = ((int64_t)bt[j >> bs_log2] << bs_log2) + (j & bs_mask);
-        v0 = ld16(cn + slot * kD + 8 * c);
-      }
-      if (j + 1 >= tok_begin && j + 1 < tok_end) {
-        const int64_t slot = ((int64_t)bt[(j + 1) >> bs_log2] << bs_log2) + ((j + 1) & bs_mask);
-        v1 = ld16(cn + slot * kD + 8 * c);
-      }
-      *reinterpret_cast<uint4*>(&c_lds[2 * pr][8 * c]) = v0;
-      *reinterpret_cast<uint4*>(&c_lds[2 * pr + 1][8 * c]) = v1;
-      uint32_t w[8];
-      interleave_pairs(v0, v1, w);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(&vt_lds[8 * c + e][2 * pr]) = w[e];
-    }
-    // Rope rows beside the latent in the row-major tile.
-    for (int idx = tid; idx < kKeyTile * (kR / 8); idx += NT) {
-      const int r = idx / (kR / 8);
-      const int c = idx - r * (kR / 8);
-      const int j = t0 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j >= tok_begin && j < tok_end) {
-        const int64_t slot = ((int64_t)bt[j >> bs_log2] << bs_log2) + (j & bs_mask);
-        v = ld16(cr + slot * kR + 8 * c);
-      }
-      *reinterpret_cast<uint4*>(&c_lds[r][kD + 8 * c]) = v;
-    }
-    __syncthreads();
+    if (t0 + kKeyTile < tok_end) issue_tile(t0 + kKeyTile, buf ^ 1);
 
     f32x4_t s[kKeyTile / 16];
 #pragma unroll
     for (int u = 0; u < kKeyTile / 16; ++u) {
+      const int r = 16 * u + l16;
       s[u] = f32x4_zero();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[u] = mfma_bf16(lds16(&c_lds[16 * u + l16][32 * ks + 8 * lg]), qf[ks], s[u]);
+      for (int ks = 0; ks < kD / 32; ++ks) s[u] = mfma_bf16(lds16(&c_lds[buf][r][32 * ks + 8 * lg]), qf[ks], s[u]);
+#pragma unroll
+      for (int ks = kD / 32; ks < KS; ++ks)
+        s[u] = mfma_bf16(lds16(&r_lds[buf][r][8 * ((4 * (ks - kD / 32) + lg) ^ rope_swz(r))]), qf[ks], s[u]);
     }
+    const bool full = t0 >= tok_begin && t0 + kKeyTile <= tok_end;
     float mt = kNegInf;
 #pragma unroll
     for (int u = 0; u < kKeyTile / 16; ++u) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = t0 + 16 * u + 4 * lg + r;
-        const float x = (j >= tok_begin && j < tok_end) ? s[u][r] * a.scale_log2e : kNegInf;
+        const float x = (full || (j >= tok_begin && j < tok_end)) ? s[u][r] : kNegInf;
         s[u][r] = x;
         mt = fmaxf(mt, x);
       }
@@ -140,15 +145,19 @@ __global__ __launch_bounds__(NW * kWave) void mla_decode_kernel(MlaArgs a) {
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mn = fmaxf(m, mt);
-    const float alpha = rescale(m, mn);
-    const float msub = mn == kNegInf ? 0.f : mn;
+    const float msc = mn == kNegInf ? 0.f : mn * c2;
+    const float alpha = m == mn ? 1.f : exp2_fast(m * c2 - msc);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
     float p8[8];
     float ls = 0.f;
 #pragma unroll
     for (int u = 0; u < kKeyTile / 16; ++u) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2_fast(s[u][r] - msub);
+        const float p = exp2_fast(fmaf(s[u][r], c2, -msc));
         p8[4 * u + r] = p;
         ls += p;
       }
@@ -156,13 +165,12 @@ __global__ __launch_bounds__(NW * kWave) void mla_decode_kernel(MlaArgs a) {
     l = l * alpha + ls;
     m = mn;
     uint4 phi, plo;
-    pack_p(p8, phi, plo);
+    pack_p_split(p8, phi, plo);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint2 x0 = lds8(&vt_lds[16 * dt + l16][4 * lg]);
-      const uint2 x1 = lds8(&vt_lds[16 * dt + l16][16 + 4 * lg]);
+      const uint2 x0 = lds_tr16(&c_lds[buf][ra][16 * dt + 4 * q4]);
+      const uint2 x1 = lds_tr16(&c_lds[buf][rb][16 * dt + 4 * q4]);
       const uint4 af = make_uint4(x0.x, x0.y, x1.x, x1.y);
-      o[dt] *= alpha;
       o[dt] = mfma_bf16(af, phi, o[dt]);
       o[dt] = mfma_bf16(af, plo, o[dt]);
     }
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(NW * kWave) void mla_decode_kernel(MlaArgs a) {
       store4(wo, 16 * dt + 4 * lg, v, PKV_F32);
     }
     if (lg == 0) {
-      a.ws_ml[(qrow * a.max_np + part) * 2 + 0] = m;
+      a.ws_ml[(qrow * a.max_np + part) * 2 + 0] = m * c2;  // log2 units, like the VALU decode
       a.ws_ml[(qrow * a.max_np + part) * 2 + 1] = lsum;
     }
   }
@@ -201,8 +209,9 @@ bool mla_decode_supported(int32_t dtype, int32_t head_dim, int32_t rope_dim, int
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   const int tiles16 = a.num_q_heads / 16;
   if (a.batch == 0) return hipSuccess;
+  if (a.blocks_per_part > kMaxBpp) return hipErrorInvalidValue;
   // Up to 8 waves (128 heads) per workgroup; the head groups tile H exactly.
-  int nw = 8;
+  int nw = a.waves_per_group > 0 ? a.waves_per_group : 8;
   while (tiles16 % nw) nw >>= 1;
   const dim3 grid(a.max_np, tiles16 / nw, a.batch);
   switch (nw) {

@@ -82,6 +82,7 @@ struct MlaArgs {
   int32_t max_blocks_per_seq, block_size_log2, blocks_per_part, max_np, window;
   float scale_log2e;
   int32_t out_dtype;
+  int32_t waves_per_group;  // 16-head waves per workgroup (0 = up to 8)
 };
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
 bool mla_decode_supported(int32_t dtype, int32_t head_dim, int32_t rope_dim, int32_t num_q_heads);

@@ -10,13 +10,25 @@
 // Work split.  One workgroup (4 waves) owns 128 "columns" of one (sequence,
 // KV head): a column is one (query row, query head) pair, ordered position-major
 // so the G heads sharing the KV head sit side by side and share each K/V tile.
-// Each wave owns two 16-column tiles.  The workgroup walks 64-key tiles: K is
-// staged row-major in LDS, V transposed (keys contiguous per dimension) so both
-// products read 16- or 8-byte LDS fragments.  S^T = K.Q^T and O^T += V^T.P^T run
-// on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; probabilities enter P.V as
-// a hi + lo bf16 pair (split_bf16) so rounding P costs no accuracy.  The online
-// softmax (running max in log2 units, v_exp_f32) is per column, which is fixed
-// per lane; the max over a tile's keys needs only two cross-lane steps.
+// Each wave owns two 16-column tiles and keeps their q in registers.
+//
+// Data path per 64-key tile.  K and V rows are copied straight from the paged
+// cache into LDS with global_load_lds (no register staging), double-buffered so
+// the next tile streams in while the current one is computed.  One wave load
+// moves 1 KiB = four 256-byte rows; it takes rows r, r+16, r+32, r+48 so that a
+// 16-row fragment read walks consecutive 1 KiB groups, padded by 32 bytes: the
+// padding at which neither fragment read has a bank conflict (measured:
+// SQ_LDS_BANK_CONFLICT is 0 at 32 bytes, nonzero at 0, 16, 48, 64 and 128).  Every fragment address is one lane constant plus an
+// immediate offset.  S^T = K.Q^T reads K fragments with ds_read_b128;
+// O^T += V^T.P^T reads the transposed V operand straight from the row-major
+// tile with ds_read_b64_tr_b16.  Both products run on v_mfma_f32_16x16x32_bf16
+// with fp32 accumulation; probabilities enter P.V as a hi + lo bf16 pair so
+// rounding P costs no accuracy.  The online softmax keeps the running max on
+// raw logits, folds scale*log2(e) into one FMA before v_exp_f32, and rescales
+// the accumulators only when some column's max moved; tiles wholly inside
+// every column's visible range skip the mask.
+#include <type_traits>
+
 #include "mfma_common.h"
 #include "pkv_internal.h"
 
@@ -27,16 +39,34 @@ constexpr int kWaves = 4;
 constexpr int kColTiles = 2;                     // 16-column tiles per wave
 constexpr int kCols = kWaves * kColTiles * 16;   // columns per workgroup
 constexpr int kKeyTile = 64;                     // keys per LDS tile
-constexpr int kKPad = 8;                         // bf16 padding per K row
-constexpr int kVPad = 4;                         // bf16 padding per V^T row
+constexpr int kMaxTableLds = 512;                // block-table entries cached in LDS
 
 template <int D>
-__global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int KS = D / 32;  // 32-wide contraction steps of Q.K
-  constexpr int DT = D / 16;  // 16-row tiles of O^T
+struct Tile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;       // rows one wave load moves
+  static constexpr int kGroups = kKeyTile / kRowsPerLoad;     // wave loads per tile and tensor
+  static constexpr int kGroupBytes = 1024 + 32;               // one load's rows plus padding
+  static constexpr int kBytes = kGroups * kGroupBytes;        // one tensor, one buffer
+  // Byte offset of (row, byte) inside a tile: load g holds rows g, g+kGroups, ...
+  static constexpr int off(int row, int byte) {
+    return (row % kGroups) * kGroupBytes + (row / kGroups) * kRowBytes + byte;
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(PrefillArgs a) {
+  using T = Tile<D>;
+  constexpr int KS = D / 32;                       // 32-wide contraction steps of Q.K
+  constexpr int DT = D / 16;                       // 16-row tiles of O^T
   constexpr int NU = kKeyTile / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKeyTile][D + kKPad];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D][kKeyTile + kVPad];
+  constexpr int LPW = T::kGroups / kWaves;         // wave loads per wave and tensor
+  // Fragment addresses split into a lane constant plus an immediate when 16-row
+  // steps map whole groups onto whole groups.
+  static_assert(T::kGroups % kWaves == 0 && (16 % T::kGroups == 0 || T::kGroups % 16 == 0), "tile layout");
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2 * T::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * T::kBytes];
+  __shared__ int32_t s_bt[kMaxTableLds];
 
   const int qt = blockIdx.x;
   const int g = blockIdx.y;
@@ -56,7 +86,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(PrefillArg
   const int col0 = qt * kCols;
   if (col0 >= ncols) return;
 
-  // This lane's columns.
+  // This lane's columns and their q fragments.
   bool cvalid[kColTiles];
   int cpos[kColTiles];
   int64_t crow[kColTiles];
@@ -67,9 +97,9 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(PrefillArg
     const int gc = col0 + (wave * kColTiles + ct) * 16 + l16;
     cvalid[ct] = gc < ncols;
     const int i = cvalid[ct] ? gc / G : 0;
-    const int hl = gc - (gc / G) * G;
+    const int hl = cvalid[ct] ? gc - i * G : 0;
     cpos[ct] = L - n + i;
-    crow[ct] = (int64_t)(q0 + i) * H + (int64_t)g * G + (cvalid[ct] ? hl : 0);
+    crow[ct] = (int64_t)(q0 + i) * H + (int64_t)g * G + hl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ct][ks] = cvalid[ct] ? ld16(q + crow[ct] * D + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
@@ -81,8 +111,47 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(PrefillArg
   const int p_hi = L - n + last_col / G;
   const int key_lo = a.window > 0 ? max(0, p_lo - a.window + 1) : 0;
   const int key_hi = p_hi + 1;
+  if (key_hi <= key_lo) return;  // malformed lengths (n > L): nothing visible
   const int t_begin = key_lo / kKeyTile;
   const int t_end = (key_hi + kKeyTile - 1) / kKeyTile;
+
+  const int bs_log2 = a.block_size_log2;
+  const int bs_mask = (1 << bs_log2) - 1;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq;
+  const int blk_lo = key_lo >> bs_log2;
+  const int nblk = ((key_hi - 1) >> bs_log2) - blk_lo + 1;
+  const bool bt_lds = nblk <= kMaxTableLds;
+  if (bt_lds)
+    for (int i = tid; i < nblk; i += kWaves * kWave) s_bt[i] = bt[blk_lo + i];
+  __syncthreads();
+
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (int64_t)g * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (int64_t)g * D;
+  const int64_t slot_stride = (int64_t)a.num_kv_heads * D;
+  // Lane constants of the loads and of the two fragment reads.
+  const int ld_row = lane / (D / 8);       // row within one wave load
+  const int ld_chunk = lane % (D / 8);     // 16-byte chunk of that row
+  const int qk_lane = T::off(l16, 16 * lg);
+  const int tr_row = 4 * lg + (l16 >> 2);  // tile row of this lane's transposed read
+  const int tr_lane = T::off(tr_row, 8 * (l16 & 3));
+
+  // Copy one 64-key tile of K and V into buffer BUF.  Keys outside
+  // [key_lo, key_hi) re-read a visible row: they are masked, and a finite row
+  // keeps 0 * v = 0 (padding table entries may point at a NaN-filled block).
+  auto issue_tile = [&](auto bufc, int tile) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int j0 = tile * kKeyTile;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int grp = wave * LPW + i;
+      const int j = min(max(j0 + grp + T::kGroups * ld_row, key_lo), key_hi - 1);
+      const int lb = j >> bs_log2;
+      const int phys = bt_lds ? s_bt[lb - blk_lo] : bt[lb];
+      const int64_t off = (((int64_t)phys << bs_log2) + (j & bs_mask)) * slot_stride + 8 * ld_chunk;
+      load_lds16(kc + off, k_lds + BUF * T::kBytes + grp * T::kGroupBytes);
+      load_lds16(vc + off, v_lds + BUF * T::kBytes + grp * T::kGroupBytes);
+    }
+  };
 
   f32x4_t o[kColTiles][DT];
   float m[kColTiles], l[kColTiles];
@@ -93,101 +162,67 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(PrefillArg
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4_zero();
   }
+  const float c2 = a.scale_log2e;
 
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq;
-  const int bs_log2 = a.block_size_log2;
-  const int bs_mask = (1 << bs_log2) - 1;
-  const int64_t slot_stride = (int64_t)a.num_kv_heads * D;
-  const int64_t head_off = (int64_t)g * D;
-
-  for (int tile = t_begin; tile < t_end; ++tile) {
+  auto compute_tile = [&](auto bufc, int tile) {
+    constexpr int BUF = decltype(bufc)::value;
+    const unsigned char* kb = k_lds + BUF * T::kBytes + qk_lane;
+    const unsigned char* vb = v_lds + BUF * T::kBytes + tr_lane;
     const int j0 = tile * kKeyTile;
-    __syncthreads();  // the previous tile is no longer read
-    // K tile, row-major: 16 lanes per key row (coalesced 16-byte chunks).
-    for (int idx = tid; idx < kKeyTile * (D / 8); idx += kWaves * kWave) {
-      const int r = idx / (D / 8);
-      const int c = idx - r * (D / 8);
-      const int j = j0 + r;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j >= key_lo && j < key_hi) {
-        const int64_t slot = ((int64_t)bt[j >> bs_log2] << bs_log2) + (j & bs_mask);
-        v = ld16(kc + slot * slot_stride + head_off + 8 * c);
-      }
-      *reinterpret_cast<uint4*>(&k_lds[r][8 * c]) = v;
-    }
-    // V tile, transposed: a lane takes two keys' chunk and writes 8 key pairs.
-    for (int idx = tid; idx < (kKeyTile / 2) * (D / 8); idx += kWaves * kWave) {
-      const int pr = idx % (kKeyTile / 2);
-      const int c = idx / (kKeyTile / 2);
-      const int j = j0 + 2 * pr;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (j >= key_lo && j < key_hi) {
-        const int64_t slot = ((int64_t)bt[j >> bs_log2] << bs_log2) + (j & bs_mask);
-        v0 = ld16(vc + slot * slot_stride + head_off + 8 * c);
-      }
-      if (j + 1 >= key_lo && j + 1 < key_hi) {
-        const int64_t slot = ((int64_t)bt[(j + 1) >> bs_log2] << bs_log2) + ((j + 1) & bs_mask);
-        v1 = ld16(vc + slot * slot_stride + head_off + 8 * c);
-      }
-      uint32_t w[8];
-      interleave_pairs(v0, v1, w);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) *reinterpret_cast<uint32_t*>(&vt_lds[8 * c + e][2 * pr]) = w[e];
-    }
-    __syncthreads();
 
     // S^T = K . Q^T
     f32x4_t s[kColTiles][NU];
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) s[ct][u] = f32x4_zero();
-#pragma unroll
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 af = lds16(&k_lds[16 * u + l16][32 * ks + 8 * lg]);
+        const uint4 af = *reinterpret_cast<const uint4*>(kb + T::off(16 * u, 64 * ks));
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) s[ct][u] = mfma_bf16(af, qf[ct][ks], s[ct][u]);
+        for (int ct = 0; ct < kColTiles; ++ct)
+          s[ct][u] = mfma_bf16(af, qf[ct][ks], ks == 0 ? f32x4_zero() : s[ct][u]);
       }
     }
 
-    // Online softmax per column.
+    // Online softmax per column (raw-logit max, scale folded into the exponent).
+    const bool full = j0 >= key_lo && j0 + kKeyTile - 1 <= p_lo && (a.window == 0 || j0 > p_hi - a.window);
 #pragma unroll
     for (int ct = 0; ct < kColTiles; ++ct) {
-      float mt = kNegInf;
+      if (!full) {
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
+        for (int u = 0; u < NU; ++u) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + 16 * u + 4 * lg + r;
-          const bool vis = cvalid[ct] && j <= cpos[ct] && (a.window == 0 || j > cpos[ct] - a.window);
-          const float x = vis ? s[ct][u][r] * a.scale_log2e : kNegInf;
-          s[ct][u][r] = x;
-          mt = fmaxf(mt, x);
+          for (int r = 0; r < 4; ++r) {
+            const int j = j0 + 16 * u + 4 * lg + r;
+            const bool vis = j <= cpos[ct] && (a.window == 0 || j > cpos[ct] - a.window);
+            s[ct][u][r] = vis ? s[ct][u][r] : kNegInf;
+          }
         }
       }
+      float mt = fmaxf(fmaxf(s[ct][0][0], s[ct][0][1]), fmaxf(s[ct][0][2], s[ct][0][3]));
+#pragma unroll
+      for (int u = 1; u < NU; ++u)
+        mt = fmaxf(mt, fmaxf(fmaxf(s[ct][u][0], s[ct][u][1]), fmaxf(s[ct][u][2], s[ct][u][3])));
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float mn = fmaxf(m[ct], mt);
-      const float alpha = rescale(m[ct], mn);
-      const float msub = mn == kNegInf ? 0.f : mn;
+      const float msc = mn == kNegInf ? 0.f : mn * c2;
+      const float alpha = m[ct] == mn ? 1.f : exp2_fast(m[ct] * c2 - msc);
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+      }
       float ls = 0.f;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2_fast(s[ct][u][r] - msub);
+          const float p = exp2_fast(fmaf(s[ct][u][r], c2, -msc));
           s[ct][u][r] = p;
           ls += p;
         }
       }
       l[ct] = l[ct] * alpha + ls;
       m[ct] = mn;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
     }
 
     // O^T += V^T . P^T, 32 keys per step, P as hi + lo bf16.
@@ -196,18 +231,14 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(PrefillArg
       uint4 phi[kColTiles], plo[kColTiles];
 #pragma unroll
       for (int ct = 0; ct < kColTiles; ++ct) {
-        float p8[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p8[r] = s[ct][2 * kk][r];
-          p8[4 + r] = s[ct][2 * kk + 1][r];
-        }
-        pack_p(p8, phi[ct], plo[ct]);
+        const float p8[8] = {s[ct][2 * kk][0],     s[ct][2 * kk][1],     s[ct][2 * kk][2],     s[ct][2 * kk][3],
+                             s[ct][2 * kk + 1][0], s[ct][2 * kk + 1][1], s[ct][2 * kk + 1][2], s[ct][2 * kk + 1][3]};
+        pack_p_split(p8, phi[ct], plo[ct]);
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint2 x0 = lds8(&vt_lds[16 * dt + l16][32 * kk + 4 * lg]);
-        const uint2 x1 = lds8(&vt_lds[16 * dt + l16][32 * kk + 16 + 4 * lg]);
+        const uint2 x0 = lds_tr16(reinterpret_cast<const uint16_t*>(vb + T::off(32 * kk, 32 * dt)));
+        const uint2 x1 = lds_tr16(reinterpret_cast<const uint16_t*>(vb + T::off(32 * kk + 16, 32 * dt)));
         const uint4 af = make_uint4(x0.x, x0.y, x1.x, x1.y);
 #pragma unroll
         for (int ct = 0; ct < kColTiles; ++ct) {
@@ -215,6 +246,22 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(PrefillArg
           o[ct][dt] = mfma_bf16(af, plo[ct], o[ct][dt]);
         }
       }
+    }
+  };
+
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  issue_tile(B0{}, t_begin);
+  for (int tile = t_begin; tile < t_end; tile += 2) {
+    wait_vmem();
+    __syncthreads();  // buffer 0 holds `tile`; nobody reads buffer 1 any more
+    if (tile + 1 < t_end) issue_tile(B1{}, tile + 1);
+    compute_tile(B0{}, tile);
+    if (tile + 1 < t_end) {
+      wait_vmem();
+      __syncthreads();  // buffer 1 holds tile+1; nobody reads buffer 0 any more
+      if (tile + 2 < t_end) issue_tile(B0{}, tile + 2);
+      compute_tile(B1{}, tile + 1);
     }
   }
 
@@ -228,7 +275,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_mfma_kernel(PrefillArg
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      float v[4] = {o[ct][dt][0] * inv, o[ct][dt][1] * inv, o[ct][dt][2] * inv, o[ct][dt][3] * inv};
+      const float v[4] = {o[ct][dt][0] * inv, o[ct][dt][1] * inv, o[ct][dt][2] * inv, o[ct][dt][3] * inv};
       store4(a.out, crow[ct] * D + 16 * dt + 4 * lg, v, a.out_dtype);
     }
   }

@@ -76,14 +76,42 @@ def out_dtype_name(t: torch.Tensor) -> str:
     return "bf16" if t.dtype == torch.bfloat16 else "f32"
 
 
-def assert_rows_close(got: torch.Tensor, ref: np.ndarray, tol: float, rows=None):
-    """Per output row: ||got - round(ref)|| / ||round(ref)|| <= tol, where round() expresses the
-    oracle's float64 result in the output dtype (bf16 by round-to-nearest-even)."""
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bfloat16 numbers at |x| (8 significant bits), for x != 0."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - 7), 0.0)
+
+
+def assert_rows_close(got: torch.Tensor, ref: np.ndarray, tol: float, rows=None, slack: float = 1e-4):
+    """Compare an attention output with the oracle's float64 result.
+
+    fp32 output: per row, ||got - ref||_2 / ||ref||_2 <= tol (accumulation error only).
+    bf16 output: (a) every element is a faithful rounding of the exact value -- within one
+    bf16 ulp of it -- up to an absolute slack of `slack` x the row's largest |ref| (fp32
+    cancellation in near-zero elements); (b) over all compared rows,
+    ||got - bf16(ref)||_F / ||bf16(ref)||_F <= tol.  A per-row norm of the bf16 output cannot
+    carry the bound: one legitimate 1-ulp rounding flip of a row's largest element already
+    costs up to ~2e-3 of a 128-element row.  Returns the worst per-row relative error."""
     g = as_f64(got)
     if rows is not None:
         g, ref = g.reshape(-1, g.shape[-1])[rows], ref.reshape(-1, ref.shape[-1])[rows]
+    g = g.reshape(-1, g.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-1])
     assert np.all(np.isfinite(g)), "non-finite output"
-    err = row_rel_err(g, round_like_output(ref, out_dtype_name(got)))
-    worst = float(err.max(initial=0.0))
-    assert worst <= tol, f"max per-row relative error {worst:.3e} > {tol:.1e}"
-    return worst
+    if out_dtype_name(got) == "f32":
+        err = row_rel_err(g, ref)
+        worst = float(err.max(initial=0.0))
+        assert worst <= tol, f"max per-row relative error {worst:.3e} > {tol:.1e}"
+        return worst
+    rmax = np.abs(ref).max(axis=-1, keepdims=True)
+    bound = bf16_ulp(ref) + slack * rmax
+    over = np.abs(g - ref) > bound
+    if over.any():
+        r, e = np.argwhere(over)[0]
+        raise AssertionError(f"{int(over.sum())} elements are not faithful roundings; first at row {r} "
+                             f"elem {e}: got {g[r, e]!r}, exact {ref[r, e]!r}, bound {bound[r, e]:.3e}")
+    rr = round_like_output(ref, "bf16")
+    total = float(np.linalg.norm(g - rr) / max(np.linalg.norm(rr), 1e-300))
+    assert total <= tol, f"aggregate relative error {total:.3e} > {tol:.1e}"
+    return float(row_rel_err(g, rr).max(initial=0.0))

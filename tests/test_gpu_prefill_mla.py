@@ -1,9 +1,10 @@
 """GPU parity of the MFMA kernels through the C ABI: chunked causal prefill and MLA absorbed
 decode, against the CPU oracle.
 
-Bars as in test_gpu_decode.py: per output row ||out - bf16(oracle)|| / ||bf16(oracle)|| <= 2e-3
-for bf16 outputs, and <= 1e-4 against the unrounded oracle in fp32-output mode (the
-probabilities enter P.V as a hi + lo bf16 pair, so only fp32 accumulation error remains).
+Bars as in test_gpu_decode.py: bf16 outputs are faithful roundings of the oracle's float64
+result with aggregate relative error <= 2e-3; in fp32-output mode every row is within 1e-4
+of the unrounded oracle (the probabilities enter P.V as a hi + lo bf16 pair, so only fp32
+accumulation error remains).
 """
 import numpy as np
 import pytest
