@@ -334,6 +334,9 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
     return fail(PKV_ERR_INVALID_ARG, "q_rope and k_rope must be given together or not at all");
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
   if (is_mla(cache)) return fail(PKV_ERR_UNSUPPORTED, "MLA prefill is not implemented");
+  if (params->max_blocks_per_seq > pkv::kPrefillMaxTableBlocks)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill: max_blocks_per_seq %d exceeds %d", params->max_blocks_per_seq,
+                pkv::kPrefillMaxTableBlocks);
   if (!pkv::prefill_mfma_supported(cache->dtype, cache->head_dim))
     return fail(PKV_ERR_UNSUPPORTED, "prefill: needs bf16 and head_dim 64 or 128 (got dtype %d, head_dim %d)",
                 cache->dtype, cache->head_dim);

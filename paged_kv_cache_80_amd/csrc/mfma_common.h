@@ -98,13 +98,44 @@ __device__ __forceinline__ void pack_p_split(const float* p8, uint4& hi, uint4& 
 }
 
 // ---- gfx950 LDS paths -------------------------------------------------------
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16*l (lds_base must be the same for the whole wave).  The copy is
-// asynchronous and counted by vmcnt.
-__device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's bytes land at lds_base + 16*l, lds_base being the same for the whole wave
+// (it travels in M0).  The copy is asynchronous and counted by vmcnt.
+//
+// It is issued from inline assembly on purpose: the compiler treats an LDS DMA
+// it can see as a store that may alias every later LDS read and puts
+// s_waitcnt vmcnt(0) in front of them, which serialises a double buffer (the
+// prefetch of tile t+1 would have to land before tile t is read).  Untracked,
+// the DMA only makes the compiler's own vmcnt waits more conservative (vector
+// memory operations retire in order), and the kernels wait for their buffers
+// explicitly with wait_vmem / wait_vmem_n before a barrier or a read.  M0 is
+// written and consumed inside the one asm statement.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void load_lds16(const void* gsrc, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)(lds_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0) as a real instruction the compiler's waitcnt pass sees: after it no
+// compiler-tracked load is outstanding, so no wait for them lands inside a loop
+// body (where it would also stall on the untracked prefetch).  gfx9 encoding:
+// vmcnt 0, expcnt 7, lgkmcnt 15.
+__device__ __forceinline__ void retire_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N == 0 || N == 8 || N == 16 || N == 24 || N == 32 || N == 36 || N == 48, "add a case");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  if constexpr (N == 36) asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
+  if constexpr (N == 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lane i receives 16-bit element (i % 4) of the 8-byte reads of lanes

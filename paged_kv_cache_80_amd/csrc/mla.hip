@@ -80,6 +80,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
   for (int ks = 0; ks < KS; ++ks)
     qf[ks] = ks < kD / 32 ? ld16(qn + qrow * kD + 32 * ks + 8 * lg)
                           : ld16(qr + qrow * kR + 32 * (ks - kD / 32) + 8 * lg);
+  retire_loads();  // q fragments are in registers before any tile is in flight
   __syncthreads();  // s_blk ready
 
   const uint16_t* cn = static_cast<const uint16_t*>(a.c_nope);

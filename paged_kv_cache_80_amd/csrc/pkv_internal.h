@@ -63,8 +63,11 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq, block_size_log2, max_q_len, window;
   float scale_log2e;
   int32_t out_dtype;
+  int32_t q_tiles;  // query tiles per (sequence, KV head); set by the launcher
 };
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
+// Widest block table the prefill kernel stages in LDS (256K tokens at 128-token blocks).
+constexpr int32_t kPrefillMaxTableBlocks = 2048;
 bool prefill_mfma_supported(int32_t dtype, int32_t head_dim);
 
 // MLA absorbed decode on MFMA (mla.hip); partials share the decode workspace layout.

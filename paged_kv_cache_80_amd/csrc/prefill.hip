@@ -39,7 +39,7 @@ constexpr int kWaves = 4;
 constexpr int kColTiles = 2;                     // 16-column tiles per wave
 constexpr int kCols = kWaves * kColTiles * 16;   // columns per workgroup
 constexpr int kKeyTile = 64;                     // keys per LDS tile
-constexpr int kMaxTableLds = 512;                // block-table entries cached in LDS
+constexpr int kMaxTableLds = kPrefillMaxTableBlocks;  // block-table entries staged in LDS
 
 template <int D>
 struct Tile {
@@ -68,12 +68,20 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[2 * T::kBytes];
   __shared__ int32_t s_bt[kMaxTableLds];
 
-  const int qt = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs round-robin by launch order; renumber them
+  // so the query tiles of one (sequence, KV head) -- which read the same K/V
+  // tiles -- run on one XCD and share its L2.
+  const int nwg = gridDim.x;                // a multiple of 8
+  const int w = blockIdx.x;
+  const int logical = (w & 7) * (nwg >> 3) + (w >> 3);
+  const int qt = logical % a.q_tiles;
+  const int gb = logical / a.q_tiles;
+  if (gb >= a.num_kv_heads * a.batch) return;  // padding workgroup
+  const int g = gb % a.num_kv_heads;
+  const int b = gb / a.num_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
@@ -105,6 +113,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
       qf[ct][ks] = cvalid[ct] ? ld16(q + crow[ct] * D + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
   }
 
+  retire_loads();  // q fragments are in registers before any tile is in flight
   // Keys any column of this workgroup can see.
   const int last_col = min(ncols - 1, col0 + kCols - 1);
   const int p_lo = L - n + col0 / G;
@@ -120,9 +129,8 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq;
   const int blk_lo = key_lo >> bs_log2;
   const int nblk = ((key_hi - 1) >> bs_log2) - blk_lo + 1;
-  const bool bt_lds = nblk <= kMaxTableLds;
-  if (bt_lds)
-    for (int i = tid; i < nblk; i += kWaves * kWave) s_bt[i] = bt[blk_lo + i];
+  // nblk <= max_blocks_per_seq <= kMaxTableLds (checked by the host).
+  for (int i = tid; i < nblk; i += kWaves * kWave) s_bt[i] = bt[blk_lo + i];
   __syncthreads();
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (int64_t)g * D;
@@ -131,6 +139,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   // Lane constants of the loads and of the two fragment reads.
   const int ld_row = lane / (D / 8);       // row within one wave load
   const int ld_chunk = lane % (D / 8);     // 16-byte chunk of that row
+  const int64_t ld_lane_off = (int64_t)T::kGroups * ld_row * slot_stride + 8 * ld_chunk;
   const int qk_lane = T::off(l16, 16 * lg);
   const int tr_row = 4 * lg + (l16 >> 2);  // tile row of this lane's transposed read
   const int tr_lane = T::off(tr_row, 8 * (l16 & 3));
@@ -141,12 +150,26 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   auto issue_tile = [&](auto bufc, int tile) {
     constexpr int BUF = decltype(bufc)::value;
     const int j0 = tile * kKeyTile;
+    if (j0 >= key_lo && j0 + kKeyTile <= key_hi && bs_log2 >= 6) {
+      // The tile lies in one block and every row is visible: one block lookup,
+      // wave-uniform base, lane offsets fixed for the whole kernel.
+      const int phys = __builtin_amdgcn_readfirstlane(s_bt[(j0 >> bs_log2) - blk_lo]);
+      const int64_t row0 = ((int64_t)phys << bs_log2) + (j0 & bs_mask);
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int grp = wave * LPW + i;
+        const int64_t base = (row0 + grp) * slot_stride;
+        load_lds16(kc + base + ld_lane_off, k_lds + BUF * T::kBytes + grp * T::kGroupBytes);
+        load_lds16(vc + base + ld_lane_off, v_lds + BUF * T::kBytes + grp * T::kGroupBytes);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int grp = wave * LPW + i;
       const int j = min(max(j0 + grp + T::kGroups * ld_row, key_lo), key_hi - 1);
       const int lb = j >> bs_log2;
-      const int phys = bt_lds ? s_bt[lb - blk_lo] : bt[lb];
+      const int phys = s_bt[lb - blk_lo];
       const int64_t off = (((int64_t)phys << bs_log2) + (j & bs_mask)) * slot_stride + 8 * ld_chunk;
       load_lds16(kc + off, k_lds + BUF * T::kBytes + grp * T::kGroupBytes);
       load_lds16(vc + off, v_lds + BUF * T::kBytes + grp * T::kGroupBytes);
@@ -287,16 +310,19 @@ bool prefill_mfma_supported(int32_t dtype, int32_t head_dim) {
   return dtype == PKV_BF16 && (head_dim == 64 || head_dim == 128);
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_mfma(const PrefillArgs& a_in, hipStream_t stream) {
+  PrefillArgs a = a_in;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t cols = (int64_t)a.max_q_len * G;
   const int64_t tiles = (cols + kCols - 1) / kCols;
   if (tiles == 0 || a.batch == 0) return hipSuccess;
-  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles, a.num_kv_heads, a.batch);
+  const int64_t total = tiles * a.num_kv_heads * a.batch;
+  const int64_t padded = (total + 7) / 8 * 8;
+  if (padded > 0x7fffffff) return hipErrorInvalidValue;
+  a.q_tiles = (int32_t)tiles;
   switch (a.head_dim) {
-    case 64: prefill_mfma_kernel<64><<<grid, kWaves * kWave, 0, stream>>>(a); break;
-    case 128: prefill_mfma_kernel<128><<<grid, kWaves * kWave, 0, stream>>>(a); break;
+    case 64: prefill_mfma_kernel<64><<<(unsigned)padded, kWaves * kWave, 0, stream>>>(a); break;
+    case 128: prefill_mfma_kernel<128><<<(unsigned)padded, kWaves * kWave, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
