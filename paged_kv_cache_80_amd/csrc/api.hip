@@ -297,7 +297,11 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
   a.scale_log2e = params->scale * pkv::kLog2e;
   a.dtype = cache->dtype;
   a.out_dtype = params->out_dtype;
-  hipError_t e = pkv::launch_decode_valu(a, st);
+  // Head groups of 4 or more are dense enough for the matrix cores (G FMAs per V
+  // element would bound the vector ALUs first); small groups, fp32 and other
+  // head sizes stay on the vector ALUs.
+  const bool use_mfma = group >= 4 && pkv::decode_mfma_supported(cache->dtype, cache->head_dim, group, plan.bpp);
+  hipError_t e = use_mfma ? pkv::launch_decode_mfma(a, st) : pkv::launch_decode_valu(a, st);
   if (e != hipSuccess) return from_hip(e, "decode launch");
   if (plan.max_np > 1) {
     e = pkv::launch_decode_combine(a.ws_o, a.ws_ml, seq_lens, params->batch, params->num_q_heads, cache->head_dim,

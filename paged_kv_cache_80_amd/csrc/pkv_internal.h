@@ -42,6 +42,9 @@ struct DecodeArgs {
   int32_t dtype, out_dtype;
 };
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
+// The same decode with the head group on the matrix cores (decode_mfma.hip).
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group, int32_t blocks_per_part);
 bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);
 
 // Second pass of split-K decode: merges the partitions of each (sequence, head).
