@@ -27,20 +27,58 @@ namespace {
 constexpr int kD = 512;        // latent width (value width)
 constexpr int kR = 64;         // rope width
 constexpr int kKeyTile = 32;
-constexpr int kRowPad = 8;     // bf16 padding per latent row in LDS
+constexpr int kRowPad = 16;    // bf16 padding per latent row in LDS (32 bytes)
 constexpr int kRow = kD + kRowPad;
 constexpr int kMaxBpp = 1024;  // table blocks per partition held in LDS
+// A column's reference maximum (log2 units) is raised only when a score exceeds
+// it by more than this; in between, probabilities up to 2^8 accumulate against
+// the stale reference, which is exact (o and l share it) and skips the O
+// rescale on almost every tile.
+constexpr float kRescaleLog2 = 8.f;
 
 __device__ __forceinline__ int rope_swz(int r) { return r & 7; }
 
-template <int NW>
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Wait for the oldest of this wave's in-flight tiles, `ahead` newer tiles
+// (each NL loads) staying in flight.
+template <int NL, int MAXA>
+__device__ __forceinline__ void wait_tile(int ahead) {
+  if constexpr (MAXA >= 2) {
+    if (ahead >= 2) { wait_vm<2 * NL>(); return; }
+  }
+  if constexpr (MAXA >= 1) {
+    if (ahead == 1) { wait_vm<NL>(); return; }
+  }
+  wait_vm<0>();
+}
+
+// global_load_lds_dwordx4 with a wave-uniform 64-bit base and a 32-bit lane
+// offset: lane l's 16 bytes at sbase + voff land at lds_base + 16*l.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)(lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// NW waves of 16 heads; NBUF key tiles in an LDS ring (NBUF - 1 in flight).
+template <int NW, int NBUF>
 __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs a) {
   constexpr int KS = (kD + kR) / 32;  // 18 contraction steps (16 latent + 2 rope)
   constexpr int DT = kD / 16;         // 32 row tiles of O^T
   constexpr int NT = NW * kWave;
-  constexpr int kLoads = kKeyTile + kKeyTile * kR / (8 * kWave);  // 32 latent + 4 rope wave loads
-  __shared__ __attribute__((aligned(16))) uint16_t c_lds[2][kKeyTile][kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t r_lds[2][kKeyTile][kR];
+  constexpr int kRopeLoads = kKeyTile * kR / (8 * kWave);  // 4 wave loads of eight rope rows
+  constexpr int kRows = kKeyTile / NW;                     // latent rows per wave and tile
+  // Wave loads per tile: rope load k goes to wave k % NW.
+  constexpr int NL_LO = kRows + (kRopeLoads + NW - 1) / NW;  // waves < kRopeLoads % NW (or all)
+  constexpr int NL_HI = kRows + kRopeLoads / NW;
+  static_assert(kKeyTile % NW == 0 && NBUF >= 2 && NBUF <= 4, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t c_lds[NBUF][kKeyTile][kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t r_lds[NBUF][kKeyTile][kR];
   __shared__ int32_t s_blk[kMaxBpp];
 
   const int part = blockIdx.x;
@@ -48,7 +86,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int H = a.num_q_heads;
@@ -85,40 +123,69 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
 
   const uint16_t* cn = static_cast<const uint16_t*>(a.c_nope);
   const uint16_t* cr = static_cast<const uint16_t*>(a.c_rope);
+  const int rope_row = lane >> 3;                                      // row within a rope load
+  const uint32_t rope_voff = 16 * ((lane & 7) ^ rope_swz(rope_row));  // 8-row steps keep r & 7
 
-  // Keys outside [tok_begin, tok_end) re-read a visible row (masked later).
-  auto slot_of = [&](int j) -> int64_t {
-    j = min(max(j, tok_begin), tok_end - 1);
-    return ((int64_t)s_blk[(j >> bs_log2) - blk0] << bs_log2) + (j & bs_mask);
-  };
+  // Copy key tile t0 into ring slot buf.  Keys outside [tok_begin, tok_end)
+  // re-read a visible row: they are masked, and a finite row keeps 0 * c = 0
+  // (spare table entries may point at a NaN-filled block).
   auto issue_tile = [&](int t0, int buf) {
-    for (int i = wave; i < kLoads; i += NW) {
-      if (i < kKeyTile) {  // one latent row per wave instruction: lane = 16-byte chunk
-        load_lds16(cn + slot_of(t0 + i) * kD + 8 * lane, &c_lds[buf][i][0]);
-      } else {             // eight rope rows per wave instruction
-        const int row0 = (i - kKeyTile) * 8;
-        const int r = row0 + (lane >> 3);
-        load_lds16(cr + slot_of(t0 + r) * kR + 8 * ((lane & 7) ^ rope_swz(r)), &r_lds[buf][row0][0]);
+    if (t0 >= tok_begin && t0 + kKeyTile <= tok_end && bs_log2 >= 5) {
+      // One block holds the whole tile and every row is visible: scalar bases.
+      const int phys = __builtin_amdgcn_readfirstlane(s_blk[(t0 >> bs_log2) - blk0]);
+      const int64_t row0 = ((int64_t)phys << bs_log2) + (t0 & bs_mask);
+      const uint16_t* cb = cn + row0 * kD;
+      const uint16_t* rb = cr + row0 * kR;
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const int i = wave + k * NW;
+        load_lds16_s(cb, (uint32_t)(i * kD * 2) + 16 * lane, &c_lds[buf][i][0]);
       }
+#pragma unroll
+      for (int k = 0; k < kRopeLoads; ++k)
+        if (k % NW == wave) load_lds16_s(rb, (uint32_t)((8 * k + rope_row) * kR * 2) + rope_voff, &r_lds[buf][8 * k][0]);
+      return;
     }
+    auto slot_of = [&](int j) -> int64_t {
+      j = min(max(j, tok_begin), tok_end - 1);
+      return ((int64_t)s_blk[(j >> bs_log2) - blk0] << bs_log2) + (j & bs_mask);
+    };
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int i = wave + k * NW;
+      load_lds16(cn + slot_of(t0 + i) * kD + 8 * lane, &c_lds[buf][i][0]);
+    }
+#pragma unroll
+    for (int k = 0; k < kRopeLoads; ++k)
+      if (k % NW == wave)
+        load_lds16(cr + slot_of(t0 + 8 * k + rope_row) * kR + rope_voff / 2, &r_lds[buf][8 * k][0]);
   };
 
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_zero();
-  float m = kNegInf, l = 0.f;
+  float mref = kNegInf, l = 0.f;  // reference maximum in log2 units, running sum
   const float c2 = a.scale_log2e;
   const int q4 = l16 & 3;
   const int ra = 4 * lg + (l16 >> 2);  // rows of this lane's transposed reads
   const int rb = ra + 16;
 
   const int t_first = tok_begin & ~(kKeyTile - 1);
-  issue_tile(t_first, 0);
-  for (int t0 = t_first; t0 < tok_end; t0 += kKeyTile) {
-    const int buf = ((t0 - t_first) / kKeyTile) & 1;
-    wait_vmem();
-    __syncthreads();
-    if (t0 + kKeyTile < tok_end) issue_tile(t0 + kKeyTile, buf ^ 1);
+  const int ntiles = (tok_end - t_first + kKeyTile - 1) / kKeyTile;
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k)
+    if (k < ntiles) issue_tile(t_first + k * kKeyTile, k);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = t_first + it * kKeyTile;
+    const int buf = it % NBUF;
+    const int ahead = min(NBUF - 2, ntiles - 1 - it);
+    if (wave < kRopeLoads % NW || kRopeLoads % NW == 0)
+      wait_tile<NL_LO, NBUF - 2>(ahead);
+    else
+      wait_tile<NL_HI, NBUF - 2>(ahead);
+    __syncthreads();  // tile it is visible; slot (it - 1) % NBUF is free
+    if (it + NBUF - 1 < ntiles) issue_tile(t0 + (NBUF - 1) * kKeyTile, (it + NBUF - 1) % NBUF);
 
     f32x4_t s[kKeyTile / 16];
 #pragma unroll
@@ -131,40 +198,43 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
       for (int ks = kD / 32; ks < KS; ++ks)
         s[u] = mfma_bf16(lds16(&r_lds[buf][r][8 * ((4 * (ks - kD / 32) + lg) ^ rope_swz(r))]), qf[ks], s[u]);
     }
-    const bool full = t0 >= tok_begin && t0 + kKeyTile <= tok_end;
+    if (!(t0 >= tok_begin && t0 + kKeyTile <= tok_end)) {
+#pragma unroll
+      for (int u = 0; u < kKeyTile / 16; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = t0 + 16 * u + 4 * lg + r;
+          s[u][r] = (j >= tok_begin && j < tok_end) ? s[u][r] : kNegInf;
+        }
+    }
     float mt = kNegInf;
 #pragma unroll
-    for (int u = 0; u < kKeyTile / 16; ++u) {
+    for (int u = 0; u < kKeyTile / 16; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = t0 + 16 * u + 4 * lg + r;
-        const float x = (full || (j >= tok_begin && j < tok_end)) ? s[u][r] : kNegInf;
-        s[u][r] = x;
-        mt = fmaxf(mt, x);
-      }
-    }
+      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[u][r]);
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    const float msc = mn == kNegInf ? 0.f : mn * c2;
-    const float alpha = m == mn ? 1.f : exp2_fast(m * c2 - msc);
-    if (__any(alpha != 1.f)) {
+    const float mts = mt * c2;
+    const bool raise = mts > mref + kRescaleLog2;
+    if (__any(raise)) {
+      const float alpha = raise ? exp2_fast(mref - mts) : 1.f;  // mref = -inf gives 0
+      if (raise) mref = mts;
+      l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
+    const float mb = mref == kNegInf ? 0.f : mref;  // no finite score yet: every p is 0
     float p8[8];
     float ls = 0.f;
 #pragma unroll
-    for (int u = 0; u < kKeyTile / 16; ++u) {
+    for (int u = 0; u < kKeyTile / 16; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2_fast(fmaf(s[u][r], c2, -msc));
+        const float p = exp2_fast(fmaf(s[u][r], c2, -mb));
         p8[4 * u + r] = p;
         ls += p;
       }
-    }
-    l = l * alpha + ls;
-    m = mn;
+    l += ls;
     uint4 phi, plo;
     pack_p_split(p8, phi, plo);
 #pragma unroll
@@ -195,7 +265,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
       store4(wo, 16 * dt + 4 * lg, v, PKV_F32);
     }
     if (lg == 0) {
-      a.ws_ml[(qrow * a.max_np + part) * 2 + 0] = m * c2;  // log2 units, like the VALU decode
+      a.ws_ml[(qrow * a.max_np + part) * 2 + 0] = mref;  // log2 units, like the VALU decode
       a.ws_ml[(qrow * a.max_np + part) * 2 + 1] = lsum;
     }
   }
@@ -216,10 +286,12 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   while (tiles16 % nw) nw >>= 1;
   const dim3 grid(a.max_np, tiles16 / nw, a.batch);
   switch (nw) {
-    case 8: mla_decode_kernel<8><<<grid, 8 * kWave, 0, stream>>>(a); break;
-    case 4: mla_decode_kernel<4><<<grid, 4 * kWave, 0, stream>>>(a); break;
-    case 2: mla_decode_kernel<2><<<grid, 2 * kWave, 0, stream>>>(a); break;
-    default: mla_decode_kernel<1><<<grid, 1 * kWave, 0, stream>>>(a); break;
+    // One 8-wave workgroup per CU can hold a 4-deep ring (152 KiB of LDS);
+    // smaller workgroups keep two slots so that several fit on a CU.
+    case 8: mla_decode_kernel<8, 4><<<grid, 8 * kWave, 0, stream>>>(a); break;
+    case 4: mla_decode_kernel<4, 2><<<grid, 4 * kWave, 0, stream>>>(a); break;
+    case 2: mla_decode_kernel<2, 2><<<grid, 2 * kWave, 0, stream>>>(a); break;
+    default: mla_decode_kernel<1, 2><<<grid, 1 * kWave, 0, stream>>>(a); break;
   }
   return hipGetLastError();
 }
