@@ -96,13 +96,40 @@ pkv_status check_params(const pkv_attn_params* p, const pkv_paged_cache* c) {
   return PKV_OK;
 }
 
-// Decode partitioning: blocks per partition and the partition count bound.
+// Decode work split.  The stream-split kernel (bf16, head_dim 128) spreads the
+// tiles of all sequences over the resident waves; the partition kernels (VALU
+// decode, MLA) split each sequence into partitions of bpp table blocks.
 struct DecodePlan {
-  int32_t bpp;
+  bool stream;
+  int32_t resident_waves;  // stream split
+  int32_t split_tiles;     // stream split: tiles per wave target (0 = all waves)
+  int32_t bpp;             // partition split
   int32_t max_np;
   size_t ws_bytes;
+  size_t ws_o_offset;
   size_t ws_ml_offset;
 };
+
+// Compute units of the current device (queried once per device; 256 when no
+// device can be queried, so that a size query without a GPU stays defined).
+int32_t device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static int32_t cached[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// The stream split needs a wave per KV head in every wave group.
+bool use_stream_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
+  return !is_mla(c) && pkv::decode_mfma_supported(c->dtype, c->head_dim, p->num_q_heads / c->num_kv_heads) &&
+         c->num_kv_heads <= pkv::decode_stream_resident_waves(device_cu_count());
+}
 
 constexpr int32_t kMaxBpp = 1024;
 
@@ -118,6 +145,17 @@ int32_t mla_waves_override() {
 }
 
 DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
+  DecodePlan plan{};
+  if (use_stream_decode(p, c)) {
+    plan.stream = true;
+    plan.resident_waves = pkv::decode_stream_resident_waves(device_cu_count());
+    plan.split_tiles = p->split_tokens / 32;  // split_tokens is a multiple of the block size (>= 16)
+    if (p->split_tokens > 0 && plan.split_tiles == 0) plan.split_tiles = 1;
+    plan.max_np = 1;
+    plan.ws_bytes = pkv::decode_stream_workspace(p->batch, p->num_q_heads, c->num_kv_heads, plan.resident_waves,
+                                                 &plan.ws_o_offset, &plan.ws_ml_offset);
+    return plan;
+  }
   const int32_t bs = c->block_size;
   int32_t span = p->max_blocks_per_seq;  // table blocks one sequence can touch
   if (p->window > 0) span = std::min<int64_t>(span, (p->window + bs - 1) / bs + 1);
@@ -141,14 +179,14 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
     bpp = (int32_t)std::max<int64_t>(1, part_tokens / bs);
   }
   bpp = std::max(1, std::min({bpp, span, kMaxBpp}));
-  DecodePlan plan;
+  // The partition index is a grid dimension limited to 65535.
+  while ((span + bpp - 1) / bpp > 65535 && bpp < kMaxBpp) bpp = std::min(2 * bpp, kMaxBpp);
   plan.bpp = bpp;
   plan.max_np = (span + bpp - 1) / bpp;
-  plan.ws_bytes = 0;
-  plan.ws_ml_offset = 0;
   if (plan.max_np > 1) {
     const size_t rows = (size_t)p->batch * p->num_q_heads * plan.max_np;
     const size_t o_bytes = (rows * c->head_dim * sizeof(float) + 255) & ~size_t(255);
+    plan.ws_o_offset = 0;
     plan.ws_ml_offset = o_bytes;
     plan.ws_bytes = o_bytes + rows * 2 * sizeof(float);
   }
@@ -232,14 +270,17 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
     return fail(PKV_ERR_INVALID_ARG, "q / q_rope / out must be 16-byte aligned");
   const int32_t group = params->num_q_heads / cache->num_kv_heads;
   const DecodePlan plan = plan_decode(params, cache);
+  if (plan.max_np > 65535) return fail(PKV_ERR_UNSUPPORTED, "decode: %d partitions exceed 65535", plan.max_np);
+  if ((int64_t)params->batch * cache->num_kv_heads > 0x7fffffff)
+    return fail(PKV_ERR_UNSUPPORTED, "decode: batch x num_kv_heads exceeds the grid");
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (plan.ws_bytes > 0 && !aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  float* ws_o = plan.max_np > 1 ? static_cast<float*>(workspace) : nullptr;
-  float* ws_ml =
-      plan.max_np > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset) : nullptr;
+  char* wsb = static_cast<char*>(workspace);
+  float* ws_o = plan.ws_bytes > 0 ? reinterpret_cast<float*>(wsb + plan.ws_o_offset) : nullptr;
+  float* ws_ml = plan.ws_bytes > 0 ? reinterpret_cast<float*>(wsb + plan.ws_ml_offset) : nullptr;
   if (is_mla(cache)) {
     if (!pkv::mla_decode_supported(cache->dtype, cache->head_dim, cache->rope_dim, params->num_q_heads))
       return fail(PKV_ERR_UNSUPPORTED, "MLA decode: needs bf16, latent 512, rope 64 and H a multiple of 16");
@@ -273,7 +314,7 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
     }
     return ok();
   }
-  if (!pkv::decode_valu_supported(cache->dtype, cache->head_dim, group))
+  if (!plan.stream && !pkv::decode_valu_supported(cache->dtype, cache->head_dim, group))
     return fail(PKV_ERR_UNSUPPORTED, "decode: dtype %d, head_dim %d, group %d not supported", cache->dtype,
                 cache->head_dim, group);
   pkv::DecodeArgs a{};
@@ -297,11 +338,15 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
   a.scale_log2e = params->scale * pkv::kLog2e;
   a.dtype = cache->dtype;
   a.out_dtype = params->out_dtype;
-  // Head groups of 4 or more are dense enough for the matrix cores (G FMAs per V
-  // element would bound the vector ALUs first); small groups, fp32 and other
-  // head sizes stay on the vector ALUs.
-  const bool use_mfma = group >= 4 && pkv::decode_mfma_supported(cache->dtype, cache->head_dim, group, plan.bpp);
-  hipError_t e = use_mfma ? pkv::launch_decode_mfma(a, st) : pkv::launch_decode_valu(a, st);
+  if (plan.stream) {
+    // bf16 with 128-wide heads: matrix-core decode over a stream split (any head
+    // group: the group is a dense contraction and every K/V row is read once).
+    a.tile_prefix = reinterpret_cast<int32_t*>(wsb);
+    a.resident_waves = plan.resident_waves;
+    a.split_tiles = plan.split_tiles;
+    return from_hip(pkv::launch_decode_stream(a, st), "decode launch");
+  }
+  hipError_t e = pkv::launch_decode_valu(a, st);
   if (e != hipSuccess) return from_hip(e, "decode launch");
   if (plan.max_np > 1) {
     e = pkv::launch_decode_combine(a.ws_o, a.ws_ml, seq_lens, params->batch, params->num_q_heads, cache->head_dim,

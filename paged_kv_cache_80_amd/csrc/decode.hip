@@ -121,9 +121,14 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
   __shared__ float s_l[kWaves][GT];
   __shared__ float s_acc[kWaves][GT][D];
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // The grid is (KV head, sequence) x partition with the KV head fastest.
+  // Workgroups are dealt to the 8 XCDs round-robin in launch order, so KV head
+  // g of every sequence runs on XCD (g + H_kv * b) mod 8: each XCD streams whole
+  // heads of whole sequences, and ragged lengths cannot pile the work of short
+  // sequences (which only have low partition indices) onto a few XCDs.
+  const int g = blockIdx.x % a.num_kv_heads;
+  const int b = blockIdx.x / a.num_kv_heads;
+  const int part = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(const float* __re
 template <typename T, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int U = GT <= 2 ? 8 : 4;
-  const dim3 grid(a.max_np, a.num_kv_heads, a.batch);
+  const dim3 grid(a.num_kv_heads * a.batch, a.max_np);
   decode_valu_kernel<T, D, GT, U><<<grid, kWaves * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }

@@ -1,26 +1,52 @@
-// decode_mfma.hip -- paged GQA decode with the head group on the matrix cores.
+// decode_mfma.hip -- paged decode on the matrix cores with a stream split.
 //
 // Same result as decode.hip (softmax(q.K^T * scale) V over the keys the newest
-// position sees, query head h reading KV head h / G), for head groups large
-// enough that the group is a dense contraction: G query heads x 32 keys x 128
-// per tile.  On the vector ALUs every V element costs G FMAs (8 for the
-// llama2-70B shape), which makes the VALU kernel issue-bound long before HBM
-// is; here S^T = K.Q^T and O^T += V^T.P^T run on v_mfma_f32_16x16x32_bf16 with
-// the G heads as MFMA columns (padded to 16), and the vector ALUs only run the
-// online softmax.
+// position sees, query head h reading KV head h / G: "KV Cache notes", the
+// attention formula, its decode form and the MHA -> MQA -> GQA section), for
+// bf16 caches with 128-wide heads.  The G query heads that share a KV head are
+// the columns of the MFMA tiles (padded to 16): S^T = K.Q^T and O^T += V^T.P^T
+// run on v_mfma_f32_16x16x32_bf16 per 32-key tile, so the vector ALUs only run
+// the online softmax and a KV row is read from HBM once for all G heads.
 //
-// Work split and data path.  One wave per (sequence, KV head, partition of
-// table blocks) -- the partitions are the split-K partitions of decode.hip and
-// share its combine.  Per 32-key tile the wave loads K straight into MFMA
-// A-operand registers (lane = key row, 8 dims at 32ks + 8lg) and V into
-// registers in row order, and keeps the next tile in flight while it computes
-// the current one (8 waves per CU, 16 KiB each).  V goes through one private
-// LDS tile so the transposed operand of O^T += V^T.P^T can be read with
-// ds_read_b64_tr_b16; its 16-byte chunks are XOR-swizzled by row & 1 so those
-// reads have at most two-way bank conflicts.  All loads are ordinary
-// compiler-tracked loads (an LDS-DMA stream was tried: at most ~96 KiB in
-// flight per CU fits the LDS, against 128 KiB here).  Probabilities enter P.V
-// as a hi + lo bf16 pair.
+// Work split (stream split).  The 32-key tiles of all sequences are laid end to
+// end as one list of C tile columns (a column is one tile position of one
+// sequence, for all H_kv heads).  The launch holds exactly the waves that are
+// resident at once, taken as NG groups of H_kv waves; group x takes the
+// contiguous run of columns [C x / NG, C (x+1) / NG) and its wave g streams KV
+// head g of those columns.  Every wave streams the same number of tiles however
+// ragged the lengths are, with no partition size to trade tail imbalance against
+// start-up cost; waves are dealt to the 8 XCDs round robin, so every XCD streams
+// the same share; and the H_kv waves of a group read the same slot rows (one
+// row holds every head of a token) at about the same time, which keeps DRAM
+// pages open.  A run crosses sequence ends: the wave then stores the partial
+// (m, l, O) of the piece of sequence b it holds as piece (x + b) H_kv + g (a
+// group boundary and a sequence boundary never produce the same x + b), and
+// stream_combine merges the pieces of each output row.  A small scan kernel
+// first turns seq_lens into the per-sequence column prefix both kernels need.
+//
+// Data path.  Each wave owns two LDS slots of one tile (K and V, 16 KiB) and
+// streams tile k + 1 into one while it computes tile k from the other.  The
+// copies are global_load_lds DMAs: 16 lanes read one 256-byte head row, a wave
+// instruction four whole rows, the way they lie in memory (loading K straight
+// into the MFMA operand layout would put 16 different rows on consecutive
+// lanes and make the L1 serve every lane separately), and no register holds a
+// tile in flight.  A DMA writes lane l's 16 bytes at 16 l of its 1 KiB LDS
+// destination, so the swizzles of the slot layout are applied on the source
+// side: the lane that fills chunk position p of row r reads logical chunk
+// p ^ swz(r).  The slots are re-read as MFMA operands: K with ds_read_b128 (its
+// chunks XOR-swizzled by row & 15 so the 16 rows of an operand read fall in
+// distinct banks), V transposed with ds_read_b64_tr_b16 (chunks swizzled by
+// 2 * (row & 7) for the same reason).  Four waves per CU with one tile in flight
+// each keep HBM saturated for plain streams, and that is what 128 KiB of slots
+// per workgroup allows.
+//
+// Online softmax.  Logits are in log2 units (scale * log2 e folded into one
+// FMA before v_exp_f32).  A column's reference maximum is raised only when a
+// tile's maximum exceeds it by more than 2^8 in probability; in between,
+// probabilities up to 256 accumulate against the stale reference, which is
+// exact (O and l share it) and skips the O rescale on almost every tile.
+// Probabilities enter P.V as a hi + lo bf16 pair (p = hi + lo + r, |r| < 2^-15
+// p), so rounding P costs no accuracy.
 #include "mfma_common.h"
 #include "pkv_internal.h"
 
@@ -29,181 +55,448 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kKeyTile = 32;
-constexpr int kRowBytes = kD * 2;                  // 256
-constexpr int kTileBytes = kKeyTile * kRowBytes;   // 8 KiB per tensor per tile
-constexpr int kMaxBpp = 256;                       // table blocks per partition held in LDS
+constexpr int kTileLog2 = 5;
+constexpr int kRowBytes = kD * 2;                 // 256: one head row of K or V
+constexpr int kTileBytes = kKeyTile * kRowBytes;  // 8 KiB: one tensor of one tile
+constexpr int kWaves = 4;                         // independent waves per workgroup
+constexpr int kSlotBytes = 2 * kTileBytes;        // K then V of one tile
+constexpr float kRescaleLog2 = 8.f;
 
-__global__ __launch_bounds__(kWave, 8) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int KS = kD / 32;
-  constexpr int DT = kD / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[kTileBytes];
-  __shared__ int32_t s_blk[kMaxBpp];
+// 16-byte chunk swizzles of row r in the staged K and V tiles.
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int lane = threadIdx.x;
+// Column maximum / sum over the four 16-lane rows of a wave (lanes l, l^16,
+// l^32, l^48): v_permlane16_swap / v_permlane32_swap exchange rows in the VALU,
+// with no LDS round trip.  With both operands equal, the two results of a swap
+// hold the value of the lane and of its partner row in some order, so their
+// maximum (sum) is the pairwise maximum (sum) on every lane.
+__device__ __forceinline__ float row4_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Scalar (SMEM) load of a value that is uniform across the wave and read-only
+// for the whole kernel.  Vector loads retire in order, so a vector load of
+// such metadata would make every wait for it also wait for the tiles in flight.
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
+// Visible keys of a sequence of length L: [lo, L), lo = L - W with a window W.
+__device__ __forceinline__ int32_t visible_lo(int32_t L, int32_t window) {
+  return (window > 0 && L > window) ? L - window : 0;
+}
+// 32-key tiles covering [lo, L), aligned to absolute positions.
+__device__ __forceinline__ int32_t seq_tiles(int32_t L, int32_t window) {
+  if (L <= 0) return 0;
+  return ((L - 1) >> kTileLog2) - (visible_lo(L, window) >> kTileLog2) + 1;
+}
+
+// Wave groups that share the C columns: every resident group, or fewer when a
+// target number of tiles per wave is given (split_tiles > 0).
+__device__ __forceinline__ int64_t stream_groups(int64_t C, int32_t resident_waves, int32_t Hkv,
+                                                 int32_t split_tiles) {
+  int64_t ng = resident_waves / Hkv;  // >= 1: the host checks H_kv <= resident waves
+  if (split_tiles > 0) ng = min(ng, max<int64_t>(1, (C + split_tiles - 1) / split_tiles));
+  return ng;
+}
+// The group whose run [C x / NG, C (x+1) / NG) holds column t.
+__device__ __forceinline__ int64_t group_of_column(int64_t t, int64_t C, int64_t ng) {
+  return ((t + 1) * ng - 1) / C;
+}
+
+// prefix[b] = sum of seq_tiles over sequences < b (prefix[B] = all columns).
+// One workgroup of 1024 threads scans 1024 sequences per step.
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ seq_lens, int32_t B,
+                                                           int32_t window, int32_t* __restrict__ prefix) {
+  __shared__ int32_t s_scan[1024];
+  const int tid = threadIdx.x;
+  int32_t run = 0;
+  if (tid == 0) prefix[0] = 0;
+  for (int32_t base = 0; base < B; base += 1024) {
+    const int32_t b = base + tid;
+    s_scan[tid] = b < B ? seq_tiles(seq_lens[b], window) : 0;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+      const int32_t add = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    if (b < B) prefix[b + 1] = run + s_scan[tid];
+    run += s_scan[1023];
+    __syncthreads();
+  }
+}
+
+// Position of a wave in the column list: sequence b, tile k of its n tiles.
+struct Cursor {
+  int32_t b, k, n;
+  int32_t lo, L;     // visible keys [lo, L) of sequence b
+  int32_t t_first;   // first key of tile 0 (lo rounded down to a tile)
+};
+
+// ONE_BLOCK: the block size is 32 or more, so a 32-key tile never straddles
+// two blocks; otherwise it is 16 and a tile spans two.
+template <bool ONE_BLOCK>
+__global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(DecodeArgs a) {
+  constexpr int KS = kD / 32;  // contraction steps of q.k
+  constexpr int DT = kD / 16;  // 16-row tiles of O^T
+  __shared__ __attribute__((aligned(16))) unsigned char lds_buf[kWaves * 2 * kSlotBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int lg = lane >> 4;
+  const int B = a.batch;
   const int H = a.num_q_heads;
-  const int G = H / a.num_kv_heads;
-  const bool cvalid = l16 < G;
-  const int64_t qrow = (int64_t)b * H + (int64_t)g * G + (cvalid ? l16 : 0);
+  const int Hkv = a.num_kv_heads;
+  const int G = H / Hkv;
+  const int32_t* __restrict__ prefix = a.tile_prefix;
 
-  const int32_t L = a.seq_lens[b];
-  const KeySpan sp = decode_span(L, a.window, a.block_size_log2, a.blocks_per_part);
-  if (part >= sp.np) {
-    if (a.max_np == 1 && sp.np == 0 && part == 0 && cvalid) {
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int dt = 0; dt < DT; ++dt) store4(a.out, qrow * kD + 16 * dt + 4 * lg, z, a.out_dtype);
+  const int64_t C = sload(prefix + B);
+  const int64_t NG = stream_groups(C, gridDim.x * kWaves, Hkv, a.split_tiles);
+  const int64_t w = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t grp = w / Hkv;  // wave-uniform
+  const int g = (int)(w - grp * Hkv);
+  if (grp >= NG) return;
+  const int64_t c_beg = C * grp / NG, c_end = C * (grp + 1) / NG;
+  if (c_beg >= c_end) return;
+
+  // Locate the first column: the sequence b with prefix[b] <= c_beg < prefix[b+1].
+  Cursor c0;
+  {
+    int lo_b = 0, hi_b = B - 1;
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (sload(prefix + mid) <= c_beg) lo_b = mid; else hi_b = mid - 1;
     }
-    return;
+    c0.b = lo_b;
+    const int32_t p0 = sload(prefix + lo_b);
+    c0.n = sload(prefix + lo_b + 1) - p0;
+    c0.k = (int)(c_beg - p0);
+    c0.L = sload(a.seq_lens + c0.b);
+    c0.lo = visible_lo(c0.L, a.window);
+    c0.t_first = c0.lo & ~(kKeyTile - 1);
   }
+  auto advance = [&](Cursor& c) {
+    if (++c.k < c.n) return;
+    c.k = 0;
+    do {  // the next sequence with a visible key (the run ends before B)
+      ++c.b;
+      c.n = c.b < B ? sload(prefix + c.b + 1) - sload(prefix + c.b) : 1;
+    } while (c.n == 0);
+    if (c.b < B) {
+      c.L = sload(a.seq_lens + c.b);
+      c.lo = visible_lo(c.L, a.window);
+      c.t_first = c.lo & ~(kKeyTile - 1);
+    }
+  };
+
+  const int64_t row_elems = (int64_t)Hkv * kD;  // elements between consecutive slots
+  const uint32_t row_bytes = (uint32_t)row_elems * 2;
   const int bs_log2 = a.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
-  const int blk0 = sp.first_blk + part * a.blocks_per_part;
-  const int nblk = min(a.blocks_per_part, ((L - 1) >> bs_log2) - blk0 + 1);
-  const int tok_begin = max(sp.lo, blk0 << bs_log2);
-  const int tok_end = min(L, (blk0 + nblk) << bs_log2);
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + blk0;
-  for (int i = lane; i < nblk; i += kWave) s_blk[i] = bt[i];
+  const uint16_t* kcache = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vcache = static_cast<const uint16_t*>(a.v_cache);
 
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  uint4 qf[KS];
+  // Lane constants.  DMA instruction i of a tensor fills rows 4i + lg; lane
+  // (l16, lg) fills chunk position l16 and so reads logical chunk l16 ^ swz(r),
+  // where r & 15 = 4(i & 3) + lg (K) and r & 7 = 4(i & 1) + lg (V).
+  uint32_t k_src[4], v_src[2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = cvalid ? ld16(q + qrow * kD + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
-  __syncthreads();
+  for (int i = 0; i < 4; ++i) k_src[i] = 16 * (l16 ^ kswz(4 * i + lg));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) v_src[i] = 16 * (l16 ^ vswz(4 * i + lg));
+  // K operand of step ks: key row 16u + l16, chunk 4ks + lg (row & 15 = l16).
+  int kr_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kr_off[ks] = l16 * kRowBytes + 16 * ((4 * ks + lg) ^ l16);
+  // V^T operand of 16-dim tile dt: row ra = 4lg + l16/4, 8 bytes at column
+  // 16dt + 4(l16 & 3); row ra + 16 has the same swizzle.
+  const int ra = 4 * lg + (l16 >> 2);
+  int vr_off[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) vr_off[dt] = ra * kRowBytes + 32 * (dt ^ (ra & 7)) + 8 * (l16 & 3);
+  unsigned char* slots = lds_buf + wave * 2 * kSlotBytes;
 
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache) + (int64_t)g * kD;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache) + (int64_t)g * kD;
-  const int64_t slot_stride = (int64_t)a.num_kv_heads * kD;
-
-  auto slot_of = [&](int j) -> int64_t {
-    j = min(max(j, tok_begin), tok_end - 1);
-    return ((int64_t)s_blk[(j >> bs_log2) - blk0] << bs_log2) + (j & bs_mask);
-  };
-  // V rows of a tile: lane takes chunk (lane & 15) of rows (lane >> 4) + 4i.
-  uint4 kr[2 * KS], vr[8];
-  auto load_tile = [&](int t0) {
+  // Copy the tile at cursor c (16 DMAs: K rows then V rows) into slot `sl`.
+  // Rows outside [lo, L) re-read a visible row of the tile: they are masked
+  // later, and a finite row keeps 0 * v = 0 (table entries outside the visible
+  // keys may point at a NaN-filled block).
+  auto issue_tile = [&](const Cursor& c, int sl) {
+    const int t0 = c.t_first + (c.k << kTileLog2);
+    const int lo_r = max(c.lo - t0, 0);
+    const int hi_r = min(c.L - t0, kKeyTile) - 1;
+    const int32_t* bt = a.block_table + (int64_t)c.b * a.max_blocks_per_seq;
+    const int64_t head_off = (int64_t)g * kD;
+    unsigned char* kdst = slots + sl * kSlotBytes;
+    unsigned char* vdst = kdst + kTileBytes;
+    if constexpr (ONE_BLOCK) {  // one table entry, a wave-uniform base and 32-bit lane offsets
+      const int32_t phys = sload(bt + (t0 >> bs_log2));
+      const int64_t row0 = ((int64_t)phys << bs_log2) + (t0 & bs_mask);
+      const uint16_t* kb = kcache + row0 * row_elems + head_off;
+      const uint16_t* vb = vcache + row0 * row_elems + head_off;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) vr[i] = ld16(vc + slot_of(t0 + 4 * i + lg) * slot_stride + 8 * l16);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t row = (uint32_t)min(max(4 * i + lg, lo_r), hi_r) * row_bytes;
+        load_lds16_s(kb, row + k_src[i & 3], kdst + 1024 * i);
+      }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t base = slot_of(t0 + 16 * u + l16) * slot_stride;
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t row = (uint32_t)min(max(4 * i + lg, lo_r), hi_r) * row_bytes;
+        load_lds16_s(vb, row + v_src[i & 1], vdst + 1024 * i);
+      }
+    } else {
+      // 16-token blocks: the tile spans blocks blk and blk + 1 (the second only
+      // if it holds a visible key); both entries are scalar reads.
+      const int blk = t0 >> bs_log2;
+      const int32_t e0 = sload(bt + blk);
+      const int32_t e1 = ((blk + 1) << bs_log2) < c.L ? sload(bt + blk + 1) : e0;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[u * KS + ks] = ld16(kc + base + 32 * ks + 8 * lg);
+      for (int i = 0; i < 8; ++i) {
+        const int j = t0 + min(max(4 * i + lg, lo_r), hi_r);
+        const int32_t phys = (j >> bs_log2) == blk ? e0 : e1;
+        const int64_t slot = ((int64_t)phys << bs_log2) + (j & bs_mask);
+        const unsigned char* kr = reinterpret_cast<const unsigned char*>(kcache + slot * row_elems + head_off);
+        const unsigned char* vr = reinterpret_cast<const unsigned char*>(vcache + slot * row_elems + head_off);
+        load_lds16(kr + k_src[i & 3], kdst + 1024 * i);
+        load_lds16(vr + v_src[i & 1], vdst + 1024 * i);
+      }
     }
   };
 
-  const int kq = l16 >> 2, q4 = l16 & 3;
-  const int ra = 4 * lg + kq;
-  const int v_off = ra * kRowBytes + 16 * ((q4 >> 1) ^ (ra & 1)) + 8 * (q4 & 1);
+  const bool cvalid = l16 < G;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+  uint4 qf[KS];
+  auto load_q = [&](const Cursor& c) {
+    const int64_t qrow = (int64_t)c.b * H + (int64_t)g * G + l16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = cvalid ? ld16(qp + qrow * kD + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
+  };
 
   f32x4_t o[DT];
+  float mref, l;  // column reference maximum (log2 units), lane partial sum
+  auto reset = [&] {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_zero();
-  float m = kNegInf, l = 0.f;
-  const float c2 = a.scale_log2e;
-  const int t_first = tok_begin & ~(kKeyTile - 1);
-
-  load_tile(t_first);
-  for (int t0 = t_first; t0 < tok_end; t0 += kKeyTile) {
-    // Stage this tile's V rows (chunk swizzled by row & 1) and keep its K.
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + lg;
-      *reinterpret_cast<uint4*>(v_lds + r * kRowBytes + 16 * (l16 ^ (r & 1))) = vr[i];
-    }
-    uint4 kcur[2 * KS];
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) kcur[i] = kr[i];
-    if (t0 + kKeyTile < tok_end) load_tile(t0 + kKeyTile);
-
-    f32x4_t s[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[u] = mfma_bf16(kcur[u * KS + ks], qf[ks], ks == 0 ? f32x4_zero() : s[u]);
-    }
-    if (!(t0 >= tok_begin && t0 + kKeyTile <= tok_end)) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = t0 + 16 * u + 4 * lg + r;
-          s[u][r] = (j >= tok_begin && j < tok_end) ? s[u][r] : kNegInf;
-        }
-    }
-    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    const float msc = mn == kNegInf ? 0.f : mn * c2;
-    const float alpha = m == mn ? 1.f : exp2_fast(m * c2 - msc);
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-    float p8[8];
-    float ls = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2_fast(fmaf(s[u][r], c2, -msc));
-        p8[4 * u + r] = p;
-        ls += p;
-      }
-    l = l * alpha + ls;
-    m = mn;
-    uint4 phi, plo;
-    pack_p_split(p8, phi, plo);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint2 x0 = lds_tr16(reinterpret_cast<const uint16_t*>(v_lds + v_off + 32 * dt));
-      const uint2 x1 = lds_tr16(reinterpret_cast<const uint16_t*>(v_lds + v_off + 16 * kRowBytes + 32 * dt));
-      const uint4 af = make_uint4(x0.x, x0.y, x1.x, x1.y);
-      o[dt] = mfma_bf16(af, phi, o[dt]);
-      o[dt] = mfma_bf16(af, plo, o[dt]);
-    }
-  }
-
-  float lsum = l;
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (!cvalid) return;
-  if (a.max_np == 1) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const float v[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
-      store4(a.out, qrow * kD + 16 * dt + 4 * lg, v, a.out_dtype);
-    }
-  } else {
-    float* wo = a.ws_o + (qrow * a.max_np + part) * kD;
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_zero();
+    mref = kNegInf;
+    l = 0.f;
+  };
+  // Store the partial of the piece of sequence c.b held, as piece (grp + b) H_kv + g.
+  auto flush = [&](const Cursor& c) {
+    const float lsum = row4_sum(l);
+    if (!cvalid) return;
+    const int64_t prow = ((grp + c.b) * Hkv + g) * G + l16;
+    float* wo = a.ws_o + prow * kD;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const float v[4] = {o[dt][0], o[dt][1], o[dt][2], o[dt][3]};
       store4(wo, 16 * dt + 4 * lg, v, PKV_F32);
     }
     if (lg == 0) {
-      a.ws_ml[(qrow * a.max_np + part) * 2 + 0] = m * c2;
-      a.ws_ml[(qrow * a.max_np + part) * 2 + 1] = lsum;
+      a.ws_ml[prow * 2 + 0] = mref;
+      a.ws_ml[prow * 2 + 1] = lsum;
     }
+  };
+
+  const float c2 = a.scale_log2e;
+  // Compute the tile at cursor c from slot `sl`.
+  auto compute = [&](const Cursor& c, int sl) {
+    const int t0 = c.t_first + (c.k << kTileLog2);
+    const unsigned char* kt = slots + sl * kSlotBytes;
+    const unsigned char* vt = kt + kTileBytes;
+
+    f32x4_t s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 af = *reinterpret_cast<const uint4*>(kt + kr_off[ks] + u * 16 * kRowBytes);
+        s[u] = mfma_bf16(af, qf[ks], ks == 0 ? f32x4_zero() : s[u]);
+      }
+    }
+    if (!(t0 >= c.lo && t0 + kKeyTile <= c.L)) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = t0 + 16 * u + 4 * lg + e;
+          s[u][e] = (j >= c.lo && j < c.L) ? s[u][e] : kNegInf;
+        }
+    }
+    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mt = row4_max(mt);
+    const float mts = mt * c2;
+    const bool raise = mts > mref + kRescaleLog2;
+    if (__any(raise)) {
+      const float alpha = raise ? exp2_fast(mref - mts) : 1.f;  // mref = -inf gives 0
+      if (raise) mref = mts;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    const float mb = mref == kNegInf ? 0.f : mref;  // no finite logit yet: every p is 0
+    float p8[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = exp2_fast(fmaf(s[u][e], c2, -mb));
+        p8[4 * u + e] = p;
+        l += p;
+      }
+    uint4 phi, plo;
+    pack_p_split(p8, phi, plo);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint2 x0 = lds_tr16(reinterpret_cast<const uint16_t*>(vt + vr_off[dt]));
+      const uint2 x1 = lds_tr16(reinterpret_cast<const uint16_t*>(vt + vr_off[dt] + 16 * kRowBytes));
+      const uint4 af = make_uint4(x0.x, x0.y, x1.x, x1.y);
+      o[dt] = mfma_bf16(af, phi, o[dt]);
+      o[dt] = mfma_bf16(af, plo, o[dt]);
+    }
+  };
+
+  // Columns c_beg .. c_end-1 in order: cc is the tile being computed, pc the
+  // one streaming in.  A sequence change stores the finished piece and loads
+  // the next q (its wait also drains the tile in flight: rarely more than once
+  // or twice per wave).
+  const int64_t ntl = c_end - c_beg;
+  Cursor cc = c0, pc = c0;
+  load_q(cc);
+  reset();
+  retire_loads();  // q is in before the first DMA: only tile copies are in flight below
+  issue_tile(pc, 0);
+  for (int64_t i = 0; i < ntl; ++i) {
+    const int sl = (int)(i & 1);
+    if (i + 1 < ntl) {
+      advance(pc);
+      issue_tile(pc, sl ^ 1);
+      wait_vm<16>();  // tile i has landed; tile i + 1's 16 copies stay in flight
+    } else {
+      wait_vm<0>();
+    }
+    compute(cc, sl);
+    if (i + 1 < ntl) {
+      const Cursor prev = cc;
+      advance(cc);
+      if (cc.k == 0) {  // a sequence ends here: store its piece, start the next one
+        flush(prev);
+        reset();
+        load_q(cc);
+        retire_loads();  // the compiler then knows q is in: no wait for it inside the loop
+      }
+    }
+  }
+  flush(cc);
+}
+
+// One wave per output row (sequence b, query head h): merge the pieces of
+// (b, h / G): M = max m_p, L = sum l_p 2^(m_p - M), out = sum o_p 2^(m_p - M) / L.
+// Lanes read the (m, l) of up to 64 pieces at once; a sequence with no visible
+// key gets a zero row.
+__global__ __launch_bounds__(kWaves * kWave) void stream_combine_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int H = a.num_q_heads;
+  if (row >= (int64_t)a.batch * H) return;
+  const int b = (int)(row / H);
+  const int h = (int)(row % H);
+  const int Hkv = a.num_kv_heads;
+  const int G = H / Hkv;
+  const int g = h / G, c = h % G;
+  const int32_t* prefix = a.tile_prefix;
+  const int32_t p0 = prefix[b];
+  const int32_t n = prefix[b + 1] - p0;
+  float O0 = 0.f, O1 = 0.f, inv = 0.f;
+  if (n > 0) {
+    const int64_t C = prefix[a.batch];
+    const int64_t NG = stream_groups(C, a.resident_waves, Hkv, a.split_tiles);
+    const int64_t xA = group_of_column(p0, C, NG), xB = group_of_column(p0 + n - 1, C, NG);
+    // Groups in [xA, xB] with an empty run (fewer columns than groups) store
+    // nothing; every other one holds a piece of sequence b.
+    auto piece_row = [&](int64_t x) { return ((x + b) * Hkv + g) * G + c; };
+    float M = kNegInf, Ls = 0.f;
+    for (int64_t x0 = xA; x0 <= xB; x0 += kWave) {  // pass 1: the maximum
+      const int64_t x = x0 + lane;
+      if (x <= xB && C * x / NG != C * (x + 1) / NG) M = fmaxf(M, a.ws_ml[piece_row(x) * 2]);
+    }
+    M = group_max<kWave>(M);
+    for (int64_t x0 = xA; x0 <= xB; x0 += kWave) {  // pass 2: weights, sum and O
+      const int64_t x = x0 + lane;
+      float f = 0.f;
+      if (x <= xB && C * x / NG != C * (x + 1) / NG) {
+        const int64_t pr = piece_row(x);
+        f = rescale(a.ws_ml[pr * 2], M);
+        Ls += a.ws_ml[pr * 2 + 1] * f;
+      }
+      const int cnt = (int)min<int64_t>(kWave, xB - x0 + 1);
+      for (int i = 0; i < cnt; ++i) {
+        const float fi = __shfl(f, i);
+        if (fi == 0.f) continue;  // empty run, or a piece that cannot contribute
+        const float2 v = *reinterpret_cast<const float2*>(a.ws_o + piece_row(x0 + i) * kD + 2 * lane);
+        O0 += v.x * fi;
+        O1 += v.y * fi;
+      }
+    }
+    Ls = group_sum<kWave>(Ls);
+    inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  }
+  const int64_t oi = row * kD + 2 * lane;
+  if (a.out_dtype == PKV_BF16) {
+    const uint32_t wd = (uint32_t)f32_to_bf16(O0 * inv) | ((uint32_t)f32_to_bf16(O1 * inv) << 16);
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + oi) = wd;
+  } else {
+    *reinterpret_cast<float2*>(static_cast<float*>(a.out) + oi) = make_float2(O0 * inv, O1 * inv);
   }
 }
 
 }  // namespace
 
-bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group, int32_t blocks_per_part) {
-  return dtype == PKV_BF16 && head_dim == kD && group >= 1 && group <= 16 && blocks_per_part <= kMaxBpp;
+bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
+  return dtype == PKV_BF16 && head_dim == kD && group >= 1 && group <= 16;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
-  if (a.blocks_per_part > kMaxBpp) return hipErrorInvalidValue;
-  const dim3 grid(a.max_np, a.num_kv_heads, a.batch);
-  decode_mfma_kernel<<<grid, kWave, 0, stream>>>(a);
+int32_t decode_stream_resident_waves(int32_t cu_count) { return cu_count * kWaves; }
+
+size_t decode_stream_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t resident_waves,
+                               size_t* ws_o_offset, size_t* ws_ml_offset) {
+  const size_t group = (size_t)(num_q_heads / num_kv_heads);
+  const size_t pieces = (size_t)resident_waves + (size_t)batch * num_kv_heads;
+  const size_t prefix_bytes = (((size_t)batch + 1) * sizeof(int32_t) + 255) & ~size_t(255);
+  const size_t o_bytes = (pieces * group * kD * sizeof(float) + 255) & ~size_t(255);
+  *ws_o_offset = prefix_bytes;
+  *ws_ml_offset = prefix_bytes + o_bytes;
+  return prefix_bytes + o_bytes + pieces * group * 2 * sizeof(float);
+}
+
+hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream) {
+  tile_prefix_kernel<<<1, 1024, 0, stream>>>(a.seq_lens, a.batch, a.window, a.tile_prefix);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)(a.resident_waves / kWaves);
+  if (a.block_size_log2 >= kTileLog2)
+    decode_stream_kernel<true><<<grid, kWaves * kWave, 0, stream>>>(a);
+  else
+    decode_stream_kernel<false><<<grid, kWaves * kWave, 0, stream>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.batch * a.num_q_heads;
+  stream_combine_kernel<<<(unsigned)((rows + kWaves - 1) / kWaves), kWaves * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 

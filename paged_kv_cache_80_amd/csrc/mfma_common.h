@@ -29,6 +29,12 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const uint4& a, const uint4& b, f32
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t mfma_bf16(const u32x4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4_t f32x4_zero() {
   f32x4_t z = {0.f, 0.f, 0.f, 0.f};
   return z;
@@ -118,7 +124,18 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, const void* lds_bas
                : "v"(gsrc), "s"(lds)
                : "memory", "m0");
 }
+// The same copy with a wave-uniform 64-bit base (SGPRs) and a 32-bit lane offset.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, const void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)(lds_base));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 // vmcnt(0) as a real instruction the compiler's waitcnt pass sees: after it no
 // compiler-tracked load is outstanding, so no wait for them lands inside a loop
 // body (where it would also stall on the untracked prefetch).  gfx9 encoding:

@@ -38,10 +38,6 @@ constexpr float kRescaleLog2 = 8.f;
 
 __device__ __forceinline__ int rope_swz(int r) { return r & 7; }
 
-// Wait until at most N vector memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-
 // Wait for the oldest of this wave's in-flight tiles, `ahead` newer tiles
 // (each NL loads) staying in flight.
 template <int NL, int MAXA>
@@ -53,16 +49,6 @@ __device__ __forceinline__ void wait_tile(int ahead) {
     if (ahead == 1) { wait_vm<NL>(); return; }
   }
   wait_vm<0>();
-}
-
-// global_load_lds_dwordx4 with a wave-uniform 64-bit base and a 32-bit lane
-// offset: lane l's 16 bytes at sbase + voff land at lds_base + 16*l.
-__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, const void* lds_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)(lds_base));
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
 }
 
 // NW waves of 16 heads; NBUF key tiles in an LDS ring (NBUF - 1 in flight).

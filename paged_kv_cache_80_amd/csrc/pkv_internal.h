@@ -40,12 +40,23 @@ struct DecodeArgs {
   int32_t window;
   float scale_log2e;
   int32_t dtype, out_dtype;
+  // Stream split (decode_mfma.hip) only: per-sequence tile prefix [batch + 1]
+  // in the workspace, the resident waves launched, and an optional target of
+  // tiles per wave (0 = spread over every resident wave).
+  int32_t* tile_prefix;
+  int32_t resident_waves;
+  int32_t split_tiles;
 };
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
-// The same decode with the head group on the matrix cores (decode_mfma.hip).
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
-bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group, int32_t blocks_per_part);
 bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);
+// The same decode on the matrix cores with a stream split (decode_mfma.hip):
+// bf16, head_dim 128, head groups up to 16.  Launches the tile scan, the decode
+// and the piece combine.
+bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
+int32_t decode_stream_resident_waves(int32_t cu_count);
+size_t decode_stream_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t resident_waves,
+                               size_t* ws_o_offset, size_t* ws_ml_offset);
+hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream);
 
 // Second pass of split-K decode: merges the partitions of each (sequence, head).
 hipError_t launch_decode_combine(const float* ws_o, const float* ws_ml, const int32_t* seq_lens,

@@ -102,14 +102,29 @@ def test_decode_workspace_too_small(lib):
 
 
 def test_workspace_size_formula(lib):
-    """Split-K partials: B*H*NP rows of head_dim floats (256-byte aligned) + (m, l) pairs."""
-    c = _cache()
+    """Partition split (the vector-ALU decode, here fp32): B*H*NP rows of head_dim floats
+    (256-byte aligned) + (m, l) pairs."""
+    c = _cache(dtype=pkv.PKV_F32)
     p = _params(split_tokens=128)  # 4 blocks per sequence -> 4 partitions
     rows = 2 * 8 * 4
     o = (rows * 128 * 4 + 255) // 256 * 256
     assert lib.paged_attn_decode_workspace(ctypes.byref(p), ctypes.byref(c)) == o + rows * 8
     p1 = _params(split_tokens=512)  # whole sequence in one partition: no workspace
     assert lib.paged_attn_decode_workspace(ctypes.byref(p1), ctypes.byref(c)) == 0
+
+
+def test_stream_workspace_layout(lib):
+    """Stream split (bf16, head_dim 128): the tile prefix (B+1 int32, 256-byte aligned), then
+    one (G x head_dim) partial and G (m, l) pairs per piece, pieces = resident waves + B*H_kv.
+    The size does not depend on split_tokens and grows by whole pieces with the batch."""
+    c = _cache()  # bf16, H_kv = 4, G = 2
+    sizes = [lib.paged_attn_decode_workspace(ctypes.byref(_params(batch=b)), ctypes.byref(c)) for b in (2, 3)]
+    assert lib.paged_attn_decode_workspace(ctypes.byref(_params(batch=2, split_tokens=256)),
+                                           ctypes.byref(c)) == sizes[0]
+    piece = 2 * 128 * 4 + 2 * 2 * 4  # one more sequence adds H_kv pieces
+    # the prefix grows by 4 bytes (within its 256-byte padding) and the partial
+    # region is 256-byte aligned, so the difference is H_kv pieces up to alignment
+    assert 0 <= sizes[1] - sizes[0] - 4 * piece < 256 + 4
 
 
 def test_write_rejects_malformed_arguments(lib):
