@@ -66,24 +66,6 @@ constexpr float kRescaleLog2 = 8.f;
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
 
-// Column maximum / sum over the four 16-lane rows of a wave (lanes l, l^16,
-// l^32, l^48): v_permlane16_swap / v_permlane32_swap exchange rows in the VALU,
-// with no LDS round trip.  With both operands equal, the two results of a swap
-// hold the value of the lane and of its partner row in some order, so their
-// maximum (sum) is the pairwise maximum (sum) on every lane.
-__device__ __forceinline__ float row4_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ float row4_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
 // Scalar (SMEM) load of a value that is uniform across the wave and read-only
 // for the whole kernel.  Vector loads retire in order, so a vector load of
 // such metadata would make every wait for it also wait for the tiles in flight.

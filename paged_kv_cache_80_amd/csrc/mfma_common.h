@@ -103,6 +103,24 @@ __device__ __forceinline__ void pack_p_split(const float* p8, uint4& hi, uint4& 
   lo.w = pack_hi16(r[6], r[7]);
 }
 
+// Column maximum / sum over the four 16-lane rows of a wave (lanes l, l^16,
+// l^32, l^48): v_permlane16_swap / v_permlane32_swap exchange rows in the VALU,
+// with no LDS round trip.  With both operands equal, the two results of a swap
+// hold the value of the lane and of its partner row in some order, so their
+// maximum (sum) is the pairwise maximum (sum) on every lane.
+__device__ __forceinline__ float row4_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // ---- gfx950 LDS paths -------------------------------------------------------
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
 // l's bytes land at lds_base + 16*l, lds_base being the same for the whole wave
