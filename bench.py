@@ -104,9 +104,15 @@ def algorithmic_bytes(case):
 # Counter-measured HBM bytes per launch of the dominant kernel, kept in the profile
 # summary together with a hash of the kernel sources they were taken on.  When the
 # sources have changed since, the figure no longer describes the kernel: null.
+_CSRC = "paged_kv_cache_80_amd/csrc/"
+_COMMON = [_CSRC + f for f in ("api.hip", "pkv_internal.h", "device_common.h", "mfma_common.h")] + ["include/pkv.h"]
+_STREAM = [_CSRC + "decode_mfma.hip"] + _COMMON
 PROFILED = {
-    "mha_decode_7b": ("decode_valu_mha_decode_7b.md",
-                      ["paged_kv_cache_80_amd/csrc/decode.hip", "paged_kv_cache_80_amd/csrc/device_common.h"]),
+    "mha_decode_7b": ("decode_stream_mha_decode_7b.md", _STREAM),
+    "gqa_decode_70b": ("decode_stream_gqa_decode_70b.md", _STREAM),
+    "gqa_decode_70b_window4096": ("decode_stream_gqa_decode_70b_window4096.md", _STREAM),
+    "chunked_prefill": ("prefill_mfma_chunked_prefill.md", [_CSRC + "prefill.hip"] + _COMMON),
+    "mla_decode": ("mla_decode_mla_decode.md", [_CSRC + "mla.hip", _CSRC + "decode.hip"] + _COMMON),
 }
 
 
