@@ -105,7 +105,7 @@ def algorithmic_bytes(case):
 # summary together with a hash of the kernel sources they were taken on.  When the
 # sources have changed since, the figure no longer describes the kernel: null.
 _CSRC = "paged_kv_cache_80_amd/csrc/"
-_COMMON = [_CSRC + f for f in ("api.hip", "pkv_internal.h", "device_common.h", "mfma_common.h")] + ["include/pkv.h"]
+_COMMON = [_CSRC + f for f in ("api.hip", "pkv_internal.h", "device_common.h", "mfma_common.h")]
 _STREAM = [_CSRC + "decode_mfma.hip"] + _COMMON
 PROFILED = {
     "mha_decode_7b": ("decode_stream_mha_decode_7b.md", _STREAM),

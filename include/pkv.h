@@ -77,8 +77,12 @@ typedef struct {
   int32_t window;             /* 0 = full attention; W > 0: a query at position p sees keys  */
                               /* p-W < j <= p ("KV Cache notes", sliding-window section)     */
   int32_t out_dtype;          /* pkv_dtype of `out` (f32 out is a diagnostic mode)           */
-  int32_t split_tokens;       /* decode only: keys per workgroup partition, a multiple of    */
-                              /* block_size; 0 = chosen by the library                       */
+  int32_t split_tokens;       /* decode only, a multiple of block_size; 0 = library choice.  */
+                              /* Partition kernels (f32, head_dim != 128, MLA): keys per     */
+                              /* workgroup partition.  Stream-split kernel (bf16, head_dim   */
+                              /* 128): the fewest keys one wave group streams, which caps    */
+                              /* the number of groups sharing the work.  Results do not      */
+                              /* depend on it beyond fp32 summation order.                   */
 } pkv_attn_params;
 
 /* slots_out[i] = block_table[batch_idx[i]][pos[i] / block_size] * block_size + pos[i] % block_size
