@@ -389,6 +389,9 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
   if (!pkv::prefill_mfma_supported(cache->dtype, cache->head_dim))
     return fail(PKV_ERR_UNSUPPORTED, "prefill: needs bf16 and head_dim 64 or 128 (got dtype %d, head_dim %d)",
                 cache->dtype, cache->head_dim);
+  // Tile loads address up to 64 slot rows from one base with 32-bit lane offsets.
+  if ((int64_t)cache->num_kv_heads * cache->head_dim * 2 > (int64_t(1) << 24))
+    return fail(PKV_ERR_UNSUPPORTED, "prefill: slot rows beyond 16 MiB (num_kv_heads %d)", cache->num_kv_heads);
   pkv::PrefillArgs a{};
   a.q = q;
   a.k_cache = cache->k_cache;

@@ -23,10 +23,11 @@
 // O^T += V^T.P^T reads the transposed V operand straight from the row-major
 // tile with ds_read_b64_tr_b16.  Both products run on v_mfma_f32_16x16x32_bf16
 // with fp32 accumulation; probabilities enter P.V as a hi + lo bf16 pair so
-// rounding P costs no accuracy.  The online softmax keeps the running max on
-// raw logits, folds scale*log2(e) into one FMA before v_exp_f32, and rescales
-// the accumulators only when some column's max moved; tiles wholly inside
-// every column's visible range skip the mask.
+// rounding P costs no accuracy.  The online softmax works in log2 units
+// (scale*log2(e) folded into one FMA before v_exp_f32), reduces a column over
+// the four 16-lane rows with permlane swaps, and raises a column's reference
+// maximum -- rescaling its accumulators -- only when a logit passes it by more
+// than 2^8; tiles wholly inside every column's visible range skip the mask.
 #include <type_traits>
 
 #include "mfma_common.h"
@@ -40,6 +41,7 @@ constexpr int kColTiles = 2;                     // 16-column tiles per wave
 constexpr int kCols = kWaves * kColTiles * 16;   // columns per workgroup
 constexpr int kKeyTile = 64;                     // keys per LDS tile
 constexpr int kMaxTableLds = kPrefillMaxTableBlocks;  // block-table entries staged in LDS
+constexpr float kRescaleLog2 = 8.f;              // lazy-rescale threshold (log2 units)
 
 template <int D>
 struct Tile {
@@ -140,6 +142,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   const int ld_row = lane / (D / 8);       // row within one wave load
   const int ld_chunk = lane % (D / 8);     // 16-byte chunk of that row
   const int64_t ld_lane_off = (int64_t)T::kGroups * ld_row * slot_stride + 8 * ld_chunk;
+  const uint32_t ld_lane_bytes = (uint32_t)(2 * ld_lane_off);  // < 2^32: rows of at most 64 KiB (checked by the host)
   const int qk_lane = T::off(l16, 16 * lg);
   const int tr_row = 4 * lg + (l16 >> 2);  // tile row of this lane's transposed read
   const int tr_lane = T::off(tr_row, 8 * (l16 & 3));
@@ -152,15 +155,15 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
     const int j0 = tile * kKeyTile;
     if (j0 >= key_lo && j0 + kKeyTile <= key_hi && bs_log2 >= 6) {
       // The tile lies in one block and every row is visible: one block lookup,
-      // wave-uniform base, lane offsets fixed for the whole kernel.
+      // a wave-uniform base in SGPRs, lane offsets fixed for the whole kernel.
       const int phys = __builtin_amdgcn_readfirstlane(s_bt[(j0 >> bs_log2) - blk_lo]);
       const int64_t row0 = ((int64_t)phys << bs_log2) + (j0 & bs_mask);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int grp = wave * LPW + i;
         const int64_t base = (row0 + grp) * slot_stride;
-        load_lds16(kc + base + ld_lane_off, k_lds + BUF * T::kBytes + grp * T::kGroupBytes);
-        load_lds16(vc + base + ld_lane_off, v_lds + BUF * T::kBytes + grp * T::kGroupBytes);
+        load_lds16_s(kc + base, ld_lane_bytes, k_lds + BUF * T::kBytes + grp * T::kGroupBytes);
+        load_lds16_s(vc + base, ld_lane_bytes, v_lds + BUF * T::kBytes + grp * T::kGroupBytes);
       }
       return;
     }
@@ -177,16 +180,28 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   };
 
   f32x4_t o[kColTiles][DT];
-  float m[kColTiles], l[kColTiles];
+  float mref[kColTiles], l[kColTiles];  // mref: reference maximum in log2 units
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) {
-    m[ct] = kNegInf;
+    mref[ct] = kNegInf;
     l[ct] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4_zero();
   }
   const float c2 = a.scale_log2e;
 
+  // One V^T fragment (16 dimensions x 32 keys) for O^T += V^T . P^T.
+  auto read_v = [&](const unsigned char* vb, int kk, int dt) {
+    const uint2 x0 = lds_tr16(reinterpret_cast<const uint16_t*>(vb + T::off(32 * kk, 32 * dt)));
+    const uint2 x1 = lds_tr16(reinterpret_cast<const uint16_t*>(vb + T::off(32 * kk + 16, 32 * dt)));
+    return make_uint4(x0.x, x0.y, x1.x, x1.y);
+  };
+
+  // Every LDS fragment is read one step ahead of the MFMAs that use it (K rows
+  // u+1 while rows u multiply, the first V fragments during the softmax, V keys
+  // kk+1 while keys kk multiply); the scheduling barriers keep the compiler from
+  // sinking the reads back next to their use, where each would stall for the
+  // full LDS latency.
   auto compute_tile = [&](auto bufc, int tile) {
     constexpr int BUF = decltype(bufc)::value;
     const unsigned char* kb = k_lds + BUF * T::kBytes + qk_lane;
@@ -195,19 +210,36 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
 
     // S^T = K . Q^T
     f32x4_t s[kColTiles][NU];
+    uint4 kf[2][KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[0][ks] = *reinterpret_cast<const uint4*>(kb + T::off(0, 64 * ks));
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+      if (u + 1 < NU) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          kf[(u + 1) & 1][ks] = *reinterpret_cast<const uint4*>(kb + T::off(16 * (u + 1), 64 * ks));
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 af = *reinterpret_cast<const uint4*>(kb + T::off(16 * u, 64 * ks));
 #pragma unroll
         for (int ct = 0; ct < kColTiles; ++ct)
-          s[ct][u] = mfma_bf16(af, qf[ct][ks], ks == 0 ? f32x4_zero() : s[ct][u]);
+          s[ct][u] = mfma_bf16(kf[u & 1][ks], qf[ct][ks], ks == 0 ? f32x4_zero() : s[ct][u]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    uint4 vf[2][DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vf[0][dt] = read_v(vb, 0, dt);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Online softmax per column (raw-logit max, scale folded into the exponent).
+    // Online softmax per column.  The reference maximum is raised only when a
+    // logit exceeds it by more than 2^8 in probability; in between,
+    // probabilities up to 256 accumulate against the stale reference, which is
+    // exact (O and l share it) and skips the O rescale on almost every tile.
     const bool full = j0 >= key_lo && j0 + kKeyTile - 1 <= p_lo && (a.window == 0 || j0 > p_hi - a.window);
+    uint4 phi[kColTiles][kKeyTile / 32], plo[kColTiles][kKeyTile / 32];
 #pragma unroll
     for (int ct = 0; ct < kColTiles; ++ct) {
       if (!full) {
@@ -221,54 +253,55 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
           }
         }
       }
-      float mt = fmaxf(fmaxf(s[ct][0][0], s[ct][0][1]), fmaxf(s[ct][0][2], s[ct][0][3]));
+      // A running chain of pairs, so that each step is one v_max3_f32.
+      float mt = s[ct][0][0];
 #pragma unroll
-      for (int u = 1; u < NU; ++u)
-        mt = fmaxf(mt, fmaxf(fmaxf(s[ct][u][0], s[ct][u][1]), fmaxf(s[ct][u][2], s[ct][u][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[ct], mt);
-      const float msc = mn == kNegInf ? 0.f : mn * c2;
-      const float alpha = m[ct] == mn ? 1.f : exp2_fast(m[ct] * c2 - msc);
-      if (__any(alpha != 1.f)) {
+      for (int e = 1; e + 1 < 4 * NU; e += 2)
+        mt = fmaxf(fmaxf(mt, s[ct][e / 4][e % 4]), s[ct][(e + 1) / 4][(e + 1) % 4]);
+      mt = fmaxf(mt, s[ct][NU - 1][3]);
+      const float mts = row4_max(mt) * c2;
+      const bool raise = mts > mref[ct] + kRescaleLog2;
+      if (__any(raise)) {
+        const float alpha = raise ? exp2_fast(mref[ct] - mts) : 1.f;  // mref = -inf gives 0
+        if (raise) mref[ct] = mts;
+        l[ct] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
       }
-      float ls = 0.f;
+      const float mb = mref[ct] == kNegInf ? 0.f : mref[ct];  // no visible key yet: every p is 0
 #pragma unroll
-      for (int u = 0; u < NU; ++u) {
+      for (int kk = 0; kk < kKeyTile / 32; ++kk) {
+        float p8[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2_fast(fmaf(s[ct][u][r], c2, -msc));
-          s[ct][u][r] = p;
-          ls += p;
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = exp2_fast(fmaf(s[ct][2 * kk + h][r], c2, -mb));
+            p8[4 * h + r] = p;
+            l[ct] += p;
+          }
+        pack_p_split(p8, phi[ct][kk], plo[ct][kk]);
       }
-      l[ct] = l[ct] * alpha + ls;
-      m[ct] = mn;
     }
+    __builtin_amdgcn_sched_barrier(0);
 
     // O^T += V^T . P^T, 32 keys per step, P as hi + lo bf16.
 #pragma unroll
     for (int kk = 0; kk < kKeyTile / 32; ++kk) {
-      uint4 phi[kColTiles], plo[kColTiles];
+      if (kk + 1 < kKeyTile / 32) {
 #pragma unroll
-      for (int ct = 0; ct < kColTiles; ++ct) {
-        const float p8[8] = {s[ct][2 * kk][0],     s[ct][2 * kk][1],     s[ct][2 * kk][2],     s[ct][2 * kk][3],
-                             s[ct][2 * kk + 1][0], s[ct][2 * kk + 1][1], s[ct][2 * kk + 1][2], s[ct][2 * kk + 1][3]};
-        pack_p_split(p8, phi[ct], plo[ct]);
+        for (int dt = 0; dt < DT; ++dt) vf[(kk + 1) & 1][dt] = read_v(vb, kk + 1, dt);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint2 x0 = lds_tr16(reinterpret_cast<const uint16_t*>(vb + T::off(32 * kk, 32 * dt)));
-        const uint2 x1 = lds_tr16(reinterpret_cast<const uint16_t*>(vb + T::off(32 * kk + 16, 32 * dt)));
-        const uint4 af = make_uint4(x0.x, x0.y, x1.x, x1.y);
 #pragma unroll
         for (int ct = 0; ct < kColTiles; ++ct) {
-          o[ct][dt] = mfma_bf16(af, phi[ct], o[ct][dt]);
-          o[ct][dt] = mfma_bf16(af, plo[ct], o[ct][dt]);
+          o[ct][dt] = mfma_bf16(vf[kk & 1][dt], phi[ct][kk], o[ct][dt]);
+          o[ct][dt] = mfma_bf16(vf[kk & 1][dt], plo[ct][kk], o[ct][dt]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -291,9 +324,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   // Normalise and store: lane holds column l16, dimensions 16*dt + 4*lg + r.
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) {
-    float ls = l[ct];
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
+    const float ls = row4_sum(l[ct]);
     if (!cvalid[ct]) continue;
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
 #pragma unroll

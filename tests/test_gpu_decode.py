@@ -244,6 +244,35 @@ def test_decode_reads_but_never_writes_the_cache(orc):
     assert (host(d.cache.k_cache).tobytes(), host(d.cache.v_cache).tobytes()) == before
 
 
+# Layouts that stress the stream split of the bf16 / head_dim 128 kernel: the tiles of all
+# sequences are dealt as contiguous runs to groups of H_kv waves, and the pieces a run
+# leaves at sequence ends are merged by the combine kernel.
+STREAM_LAYOUTS = [
+    # name, B, H, Hkv, bs, max_blocks, seq_lens or len_range, window
+    ("one long sequence, a piece per group", 1, 8, 1, 128, 256, [32768], 0),
+    ("fewer tiles than groups", 3, 8, 2, 16, 4, [5, 40, 33], 0),
+    ("H_kv not dividing the resident waves", 4, 15, 3, 128, 12, (1, 1536), 0),
+    ("64 KV heads per group", 20, 64, 64, 128, 16, (1, 2048), 0),
+    ("window with 16-token blocks", 7, 16, 4, 16, 200, (1, 3200), 100),
+    ("many short sequences", 600, 8, 4, 32, 3, (0, 96), 0),
+    ("lengths on tile and block edges", 8, 16, 8, 64, 8, [32, 33, 63, 64, 65, 127, 128, 512], 0),
+]
+
+
+@pytest.mark.parametrize("layout", STREAM_LAYOUTS, ids=[x[0] for x in STREAM_LAYOUTS])
+@pytest.mark.parametrize("split", [0, 2])
+def test_stream_split_layouts(orc, layout, split):
+    name, B, H, Hkv, bs, mb, lens, w = layout
+    kw = {"seq_lens": np.array(lens, dtype=np.int32)} if isinstance(lens, list) else {"len_range": lens}
+    case = workloads.decode_case(B * 7 + Hkv + split, B, H, Hkv, 128, "bf16", block_size=bs, max_blocks=mb,
+                                 window=w, null_block=True, **kw)
+    ref, _, _ = oracle_run(orc, case)
+    out, _ = DeviceCase(case).run(out_dtype=torch.float32, split_tokens=split * bs)
+    assert_rows_close(out, ref, ACC_TOL)
+    out, _ = DeviceCase(case).run(split_tokens=split * bs)
+    assert_rows_close(out, ref, BF16_TOL)
+
+
 def test_scale_without_default_is_rejected():
     import paged_kv_cache_80_amd as pkv
     case = workloads.decode_case(46, 2, 4, 4, 128, "bf16", block_size=128, max_blocks=2,
