@@ -21,8 +21,10 @@
 // pages open.  A run crosses sequence ends: the wave then stores the partial
 // (m, l, O) of the piece of sequence b it holds as piece (x + b) H_kv + g (a
 // group boundary and a sequence boundary never produce the same x + b), and
-// stream_combine merges the pieces of each output row.  A small scan kernel
-// first turns seq_lens into the per-sequence column prefix both kernels need.
+// stream_combine merges the pieces of each output row.  Both kernels need the
+// per-sequence column prefix of seq_lens: each decode workgroup scans it into
+// LDS at start (workgroup 0 also stores it for the combine), or, for batches
+// of 2048 sequences and more, a small scan kernel writes it first.
 //
 // Data path.  Each wave owns two LDS slots of one tile (K and V, 16 KiB) and
 // streams tile k + 1 into one while it computes tile k from the other.  The
@@ -61,6 +63,7 @@ constexpr int kTileBytes = kKeyTile * kRowBytes;  // 8 KiB: one tensor of one ti
 constexpr int kWaves = 4;                         // independent waves per workgroup
 constexpr int kSlotBytes = 2 * kTileBytes;        // K then V of one tile
 constexpr float kRescaleLog2 = 8.f;
+constexpr int kLdsPrefix = 2048;                   // batch + 1 up to this: prefix scanned in LDS
 
 // 16-byte chunk swizzles of row r in the staged K and V tiles.
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
@@ -130,11 +133,16 @@ struct Cursor {
 
 // ONE_BLOCK: the block size is 32 or more, so a 32-key tile never straddles
 // two blocks; otherwise it is 16 and a tile spans two.
-template <bool ONE_BLOCK>
+// LDS_PREFIX: every workgroup scans seq_lens into its own LDS copy of the
+// column prefix (batch + 1 <= kLdsPrefix) and workgroup 0 also stores it for
+// the combine; otherwise tile_prefix_kernel has written it to the workspace.
+template <bool ONE_BLOCK, bool LDS_PREFIX>
 __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(DecodeArgs a) {
   constexpr int KS = kD / 32;  // contraction steps of q.k
   constexpr int DT = kD / 16;  // 16-row tiles of O^T
   __shared__ __attribute__((aligned(16))) unsigned char lds_buf[kWaves * 2 * kSlotBytes];
+  __shared__ int32_t s_prefix[LDS_PREFIX ? kLdsPrefix : 1];
+  __shared__ int32_t s_wave_sum[kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -145,9 +153,47 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
   const int H = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = H / Hkv;
-  const int32_t* __restrict__ prefix = a.tile_prefix;
+  if constexpr (LDS_PREFIX) {
+    // Thread t owns sequences [kPerThread t, kPerThread (t + 1)): local sums,
+    // a wave scan of the thread totals, then the waves' totals through LDS.
+    constexpr int kPerThread = kLdsPrefix / (kWaves * kWave);
+    int32_t incl[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)  // all loads first (clamped: B >= 1), then the sums
+      incl[j] = a.seq_lens[min(kPerThread * tid + j, B - 1)];
+    int32_t run = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      run += kPerThread * tid + j < B ? seq_tiles(incl[j], a.window) : 0;
+      incl[j] = run;
+    }
+    int32_t x = run;  // inclusive scan of the thread totals over the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) s_wave_sum[wave] = x;
+    __syncthreads();
+    int32_t excl = x - run;
+    for (int w2 = 0; w2 < wave; ++w2) excl += s_wave_sum[w2];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int b = kPerThread * tid + j;
+      if (b < B) s_prefix[b + 1] = excl + incl[j];
+    }
+    if (tid == 0) s_prefix[0] = 0;
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = tid; i <= B; i += kWaves * kWave) a.tile_prefix[i] = s_prefix[i];
+  }
+  // prefix[i]: columns of the sequences before i (prefix[B] = all columns).
+  auto prefix_at = [&](int i) -> int32_t {
+    if constexpr (LDS_PREFIX) return __builtin_amdgcn_readfirstlane(s_prefix[i]);
+    else return sload(a.tile_prefix + i);
+  };
 
-  const int64_t C = sload(prefix + B);
+  const int64_t C = prefix_at(B);
   const int64_t NG = stream_groups(C, gridDim.x * kWaves, Hkv, a.split_tiles);
   const int64_t w = (int64_t)blockIdx.x * kWaves + wave;
   const int64_t grp = w / Hkv;  // wave-uniform
@@ -162,11 +208,11 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
     int lo_b = 0, hi_b = B - 1;
     while (lo_b < hi_b) {
       const int mid = (lo_b + hi_b + 1) >> 1;
-      if (sload(prefix + mid) <= c_beg) lo_b = mid; else hi_b = mid - 1;
+      if (prefix_at(mid) <= c_beg) lo_b = mid; else hi_b = mid - 1;
     }
     c0.b = lo_b;
-    const int32_t p0 = sload(prefix + lo_b);
-    c0.n = sload(prefix + lo_b + 1) - p0;
+    const int32_t p0 = prefix_at(lo_b);
+    c0.n = prefix_at(lo_b + 1) - p0;
     c0.k = (int)(c_beg - p0);
     c0.L = sload(a.seq_lens + c0.b);
     c0.lo = visible_lo(c0.L, a.window);
@@ -177,7 +223,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
     c.k = 0;
     do {  // the next sequence with a visible key (the run ends before B)
       ++c.b;
-      c.n = c.b < B ? sload(prefix + c.b + 1) - sload(prefix + c.b) : 1;
+      c.n = c.b < B ? prefix_at(c.b + 1) - prefix_at(c.b) : 1;
     } while (c.n == 0);
     if (c.b < B) {
       c.L = sload(a.seq_lens + c.b);
@@ -426,13 +472,25 @@ __global__ __launch_bounds__(kWaves * kWave) void stream_combine_kernel(DecodeAr
         f = rescale(a.ws_ml[pr * 2], M);
         Ls += a.ws_ml[pr * 2 + 1] * f;
       }
+      // Eight pieces' loads in flight at a time: the loads are unconditional
+      // (clamped to the last piece of the chunk, all inside the workspace) and a
+      // zero weight -- an empty run whose slot holds stale data, or a piece
+      // that cannot contribute -- selects nothing rather than multiplying.
       const int cnt = (int)min<int64_t>(kWave, xB - x0 + 1);
-      for (int i = 0; i < cnt; ++i) {
-        const float fi = __shfl(f, i);
-        if (fi == 0.f) continue;  // empty run, or a piece that cannot contribute
-        const float2 v = *reinterpret_cast<const float2*>(a.ws_o + piece_row(x0 + i) * kD + 2 * lane);
-        O0 += v.x * fi;
-        O1 += v.y * fi;
+      for (int i0 = 0; i0 < cnt; i0 += 8) {
+        float2 v[8];
+        float w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = min(i0 + k, cnt - 1);
+          w[k] = i0 + k < cnt ? __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(f), i)) : 0.f;
+          v[k] = *reinterpret_cast<const float2*>(a.ws_o + piece_row(x0 + i) * kD + 2 * lane);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          O0 = w[k] != 0.f ? fmaf(v[k].x, w[k], O0) : O0;
+          O1 = w[k] != 0.f ? fmaf(v[k].y, w[k], O1) : O1;
+        }
       }
     }
     Ls = group_sum<kWave>(Ls);
@@ -467,15 +525,24 @@ size_t decode_stream_workspace(int32_t batch, int32_t num_q_heads, int32_t num_k
 }
 
 hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream) {
-  tile_prefix_kernel<<<1, 1024, 0, stream>>>(a.seq_lens, a.batch, a.window, a.tile_prefix);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (a.batch <= 0) return hipSuccess;
+  const bool lds_prefix = (int64_t)a.batch + 1 <= kLdsPrefix;
+  if (!lds_prefix) {
+    tile_prefix_kernel<<<1, 1024, 0, stream>>>(a.seq_lens, a.batch, a.window, a.tile_prefix);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const unsigned grid = (unsigned)(a.resident_waves / kWaves);
-  if (a.block_size_log2 >= kTileLog2)
-    decode_stream_kernel<true><<<grid, kWaves * kWave, 0, stream>>>(a);
+  const bool one_block = a.block_size_log2 >= kTileLog2;
+  if (lds_prefix && one_block)
+    decode_stream_kernel<true, true><<<grid, kWaves * kWave, 0, stream>>>(a);
+  else if (lds_prefix)
+    decode_stream_kernel<false, true><<<grid, kWaves * kWave, 0, stream>>>(a);
+  else if (one_block)
+    decode_stream_kernel<true, false><<<grid, kWaves * kWave, 0, stream>>>(a);
   else
-    decode_stream_kernel<false><<<grid, kWaves * kWave, 0, stream>>>(a);
-  e = hipGetLastError();
+    decode_stream_kernel<false, false><<<grid, kWaves * kWave, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.batch * a.num_q_heads;
   stream_combine_kernel<<<(unsigned)((rows + kWaves - 1) / kWaves), kWaves * kWave, 0, stream>>>(a);

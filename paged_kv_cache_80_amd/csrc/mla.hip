@@ -30,6 +30,10 @@ constexpr int kKeyTile = 32;
 constexpr int kRowPad = 16;    // bf16 padding per latent row in LDS (32 bytes)
 constexpr int kRow = kD + kRowPad;
 constexpr int kMaxBpp = 1024;  // table blocks per partition held in LDS
+// Fragment reads issued ahead of their MFMAs (Q.K steps, P.V row tiles): two
+// each is what the 8-wave kernel's registers hold next to q and O.
+constexpr int kQkAhead = 2;
+constexpr int kPvAhead = 2;
 // A column's reference maximum (log2 units) is raised only when a score exceeds
 // it by more than this; in between, probabilities up to 2^8 accumulate against
 // the stale reference, which is exact (o and l share it) and skips the O
@@ -51,8 +55,9 @@ __device__ __forceinline__ void wait_tile(int ahead) {
   wait_vm<0>();
 }
 
-// NW waves of 16 heads; NBUF key tiles in an LDS ring (NBUF - 1 in flight).
-template <int NW, int NBUF>
+// NW waves of 16 heads; NBUF key tiles in an LDS ring (NBUF - 1 in flight);
+// QD / PD fragment reads in flight ahead of the Q.K / P.V MFMAs.
+template <int NW, int NBUF, int QD, int PD>
 __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs a) {
   constexpr int KS = (kD + kR) / 32;  // 18 contraction steps (16 latent + 2 rope)
   constexpr int DT = kD / 16;         // 32 row tiles of O^T
@@ -173,16 +178,26 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
     __syncthreads();  // tile it is visible; slot (it - 1) % NBUF is free
     if (it + NBUF - 1 < ntiles) issue_tile(t0 + (NBUF - 1) * kKeyTile, (it + NBUF - 1) % NBUF);
 
-    f32x4_t s[kKeyTile / 16];
+    // S^T = C.Q^T over 18 contraction steps for both 16-key halves, the steps
+    // of the two halves interleaved; each fragment is read QD steps ahead of
+    // its MFMA (scheduling barriers keep the read there), so the LDS latency
+    // overlaps the MFMAs instead of stalling every step.
+    constexpr int NF = 2 * KS;
+    auto c_frag = [&](int f) {
+      const int ks = f >> 1, r = 16 * (f & 1) + l16;
+      return ks < kD / 32 ? lds16(&c_lds[buf][r][32 * ks + 8 * lg])
+                          : lds16(&r_lds[buf][r][8 * ((4 * (ks - kD / 32) + lg) ^ rope_swz(r))]);
+    };
+    f32x4_t s[2] = {f32x4_zero(), f32x4_zero()};
+    uint4 cf[QD + 1];
 #pragma unroll
-    for (int u = 0; u < kKeyTile / 16; ++u) {
-      const int r = 16 * u + l16;
-      s[u] = f32x4_zero();
+    for (int f = 0; f < QD; ++f) cf[f] = c_frag(f);
 #pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) s[u] = mfma_bf16(lds16(&c_lds[buf][r][32 * ks + 8 * lg]), qf[ks], s[u]);
-#pragma unroll
-      for (int ks = kD / 32; ks < KS; ++ks)
-        s[u] = mfma_bf16(lds16(&r_lds[buf][r][8 * ((4 * (ks - kD / 32) + lg) ^ rope_swz(r))]), qf[ks], s[u]);
+    for (int f = 0; f < NF; ++f) {
+      if (f + QD < NF) cf[(f + QD) % (QD + 1)] = c_frag(f + QD);
+      __builtin_amdgcn_sched_barrier(0);
+      s[f & 1] = mfma_bf16(cf[f % (QD + 1)], qf[f >> 1], s[f & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (!(t0 >= tok_begin && t0 + kKeyTile <= tok_end)) {
 #pragma unroll
@@ -198,9 +213,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
     for (int u = 0; u < kKeyTile / 16; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[u][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mts = mt * c2;
+    const float mts = row4_max(mt) * c2;
     const bool raise = mts > mref + kRescaleLog2;
     if (__any(raise)) {
       const float alpha = raise ? exp2_fast(mref - mts) : 1.f;  // mref = -inf gives 0
@@ -223,19 +236,26 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
     l += ls;
     uint4 phi, plo;
     pack_p_split(p8, phi, plo);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    // O^T += C^T.P^T: the transposed fragment of row tile dt is read PD tiles ahead.
+    auto v_frag = [&](int dt) {
       const uint2 x0 = lds_tr16(&c_lds[buf][ra][16 * dt + 4 * q4]);
       const uint2 x1 = lds_tr16(&c_lds[buf][rb][16 * dt + 4 * q4]);
-      const uint4 af = make_uint4(x0.x, x0.y, x1.x, x1.y);
-      o[dt] = mfma_bf16(af, phi, o[dt]);
-      o[dt] = mfma_bf16(af, plo, o[dt]);
+      return make_uint4(x0.x, x0.y, x1.x, x1.y);
+    };
+    uint4 vf[PD + 1];
+#pragma unroll
+    for (int dt = 0; dt < PD; ++dt) vf[dt] = v_frag(dt);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      if (dt + PD < DT) vf[(dt + PD) % (PD + 1)] = v_frag(dt + PD);
+      __builtin_amdgcn_sched_barrier(0);
+      o[dt] = mfma_bf16(vf[dt % (PD + 1)], phi, o[dt]);
+      o[dt] = mfma_bf16(vf[dt % (PD + 1)], plo, o[dt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  float lsum = l;
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  const float lsum = row4_sum(l);
   if (a.max_np == 1) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
@@ -274,10 +294,10 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   switch (nw) {
     // One 8-wave workgroup per CU can hold a 4-deep ring (152 KiB of LDS);
     // smaller workgroups keep two slots so that several fit on a CU.
-    case 8: mla_decode_kernel<8, 4><<<grid, 8 * kWave, 0, stream>>>(a); break;
-    case 4: mla_decode_kernel<4, 2><<<grid, 4 * kWave, 0, stream>>>(a); break;
-    case 2: mla_decode_kernel<2, 2><<<grid, 2 * kWave, 0, stream>>>(a); break;
-    default: mla_decode_kernel<1, 2><<<grid, 1 * kWave, 0, stream>>>(a); break;
+    case 8: mla_decode_kernel<8, 4, kQkAhead, kPvAhead><<<grid, 8 * kWave, 0, stream>>>(a); break;
+    case 4: mla_decode_kernel<4, 2, kQkAhead, kPvAhead><<<grid, 4 * kWave, 0, stream>>>(a); break;
+    case 2: mla_decode_kernel<2, 2, kQkAhead, kPvAhead><<<grid, 2 * kWave, 0, stream>>>(a); break;
+    default: mla_decode_kernel<1, 2, kQkAhead, kPvAhead><<<grid, 1 * kWave, 0, stream>>>(a); break;
   }
   return hipGetLastError();
 }

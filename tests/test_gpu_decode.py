@@ -255,6 +255,7 @@ STREAM_LAYOUTS = [
     ("64 KV heads per group", 20, 64, 64, 128, 16, (1, 2048), 0),
     ("window with 16-token blocks", 7, 16, 4, 16, 200, (1, 3200), 100),
     ("many short sequences", 600, 8, 4, 32, 3, (0, 96), 0),
+    ("batch past the in-LDS column prefix", 2100, 4, 2, 16, 4, (0, 64), 0),
     ("lengths on tile and block edges", 8, 16, 8, 64, 8, [32, 33, 63, 64, 65, 127, 128, 512], 0),
 ]
 
