@@ -138,7 +138,11 @@ size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_pag
  *   seq_lens_kv  : [batch], cached + new keys (n_b <= seq_lens_kv[b]); the new rows
  *                  must already be in the cache (kv_cache_write first)
  *   max_q_len    : an upper bound of every n_b (sizes the grid)
- *   out          : [total_q, H, head_dim] in params->out_dtype */
+ *   out          : [total_q, H, head_dim] in params->out_dtype
+ * Standard caches need bf16 and head_dim 64 or 128.  MLA caches (absorbed form,
+ * the same constraints as decode) also cover multi-token decode (n_b of 2-4):
+ * every query row is computed over all the keys it sees by one workgroup, so
+ * no workspace is used and a row may span at most 1024 table blocks. */
 pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged_cache* cache,
                               const int32_t* block_table, const int32_t* cu_seqlens_q,
                               const int32_t* seq_lens_kv, int32_t total_q, int32_t max_q_len,

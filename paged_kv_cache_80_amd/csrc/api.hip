@@ -304,6 +304,7 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
     m.scale_log2e = params->scale * pkv::kLog2e;
     m.out_dtype = params->out_dtype;
     m.waves_per_group = mla_waves_override();
+    m.rows = params->batch;
     hipError_t e = pkv::launch_mla_decode(m, st);
     if (e != hipSuccess) return from_hip(e, "MLA decode launch");
     if (plan.max_np > 1) {
@@ -382,7 +383,39 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
   if ((q_rope != nullptr) != is_mla(cache))
     return fail(PKV_ERR_INVALID_ARG, "q_rope and k_rope must be given together or not at all");
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
-  if (is_mla(cache)) return fail(PKV_ERR_UNSUPPORTED, "MLA prefill is not implemented");
+  if (is_mla(cache)) {
+    // Absorbed-form prefill: every query row runs the MLA decode kernel as a
+    // decode over the keys up to its position, whole (one partition per row:
+    // rows x head groups give the workgroups, and no partials are kept).
+    if (!pkv::mla_decode_supported(cache->dtype, cache->head_dim, cache->rope_dim, params->num_q_heads))
+      return fail(PKV_ERR_UNSUPPORTED, "MLA prefill: needs bf16, latent 512, rope 64 and H a multiple of 16");
+    if (!q_rope || !aligned16(q_rope)) return fail(PKV_ERR_INVALID_ARG, "MLA prefill: q_rope must be 16-byte aligned");
+    int32_t span = params->max_blocks_per_seq;
+    if (params->window > 0) span = std::min<int64_t>(span, (params->window + cache->block_size - 1) / cache->block_size + 1);
+    if (span > kMaxBpp)
+      return fail(PKV_ERR_UNSUPPORTED, "MLA prefill: a row may span %d blocks, more than %d", span, kMaxBpp);
+    pkv::MlaArgs m{};
+    m.q = q;
+    m.q_rope = q_rope;
+    m.c_nope = cache->k_cache;
+    m.c_rope = cache->k_rope_cache;
+    m.block_table = block_table;
+    m.seq_lens = seq_lens_kv;
+    m.out = out;
+    m.batch = params->batch;
+    m.num_q_heads = params->num_q_heads;
+    m.max_blocks_per_seq = params->max_blocks_per_seq;
+    m.block_size_log2 = log2i(cache->block_size);
+    m.blocks_per_part = span;
+    m.max_np = 1;
+    m.window = params->window;
+    m.scale_log2e = params->scale * pkv::kLog2e;
+    m.out_dtype = params->out_dtype;
+    m.waves_per_group = mla_waves_override();
+    m.cu_seqlens_q = cu_seqlens_q;
+    m.rows = total_q;
+    return from_hip(pkv::launch_mla_decode(m, static_cast<hipStream_t>(stream)), "MLA prefill launch");
+  }
   if (params->max_blocks_per_seq > pkv::kPrefillMaxTableBlocks)
     return fail(PKV_ERR_UNSUPPORTED, "prefill: max_blocks_per_seq %d exceeds %d", params->max_blocks_per_seq,
                 pkv::kPrefillMaxTableBlocks);

@@ -18,6 +18,8 @@
 // transposed operand of O^T += C^T.P^T -- no second copy.  Partials (m, l, o)
 // of each partition go to the workspace and the split-K combine of decode.hip
 // merges them, exactly as for standard decode.
+#include <algorithm>
+
 #include "mfma_common.h"
 #include "pkv_internal.h"
 
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
 
   const int part = blockIdx.x;
   const int hg = blockIdx.y;
-  const int b = blockIdx.z;
+  const int row = a.row0 + (int)blockIdx.z;  // query row: the sequence (decode) or a row of q (prefill)
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -82,9 +84,26 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
   const int lg = lane >> 4;
   const int H = a.num_q_heads;
   const int head = (hg * NW + wave) * 16 + l16;
-  const int64_t qrow = (int64_t)b * H + head;
+  const int64_t qrow = (int64_t)row * H + head;
 
-  const int32_t L = a.seq_lens[b];
+  // Decode: row b attends to the L = seq_lens[b] keys of sequence b.  Prefill:
+  // row i of sequence b (cu[b] <= row < cu[b+1], n = cu[b+1] - cu[b] new rows)
+  // sits at position seq_lens[b] - n + i and attends to the keys up to it, i.e.
+  // it is a decode of length seq_lens[b] - n + i + 1 over sequence b's table.
+  int b = row;
+  int32_t L;
+  if (a.cu_seqlens_q) {
+    const int32_t* cu = a.cu_seqlens_q;
+    int lo_b = 0, hi_b = a.batch - 1;  // the last b with cu[b] <= row
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (cu[mid] <= row) lo_b = mid; else hi_b = mid - 1;
+    }
+    b = lo_b;
+    L = a.seq_lens[b] - (cu[b + 1] - cu[b]) + (row - cu[b]) + 1;
+  } else {
+    L = a.seq_lens[b];
+  }
   const KeySpan sp = decode_span(L, a.window, a.block_size_log2, a.blocks_per_part);
   if (part >= sp.np) {
     if (a.max_np == 1 && sp.np == 0 && part == 0) {
@@ -285,21 +304,28 @@ bool mla_decode_supported(int32_t dtype, int32_t head_dim, int32_t rope_dim, int
 
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   const int tiles16 = a.num_q_heads / 16;
-  if (a.batch == 0) return hipSuccess;
+  if (a.batch == 0 || a.rows == 0) return hipSuccess;
   if (a.blocks_per_part > kMaxBpp) return hipErrorInvalidValue;
   // Up to 8 waves (128 heads) per workgroup; the head groups tile H exactly.
   int nw = a.waves_per_group > 0 ? a.waves_per_group : 8;
   while (tiles16 % nw) nw >>= 1;
-  const dim3 grid(a.max_np, tiles16 / nw, a.batch);
-  switch (nw) {
-    // One 8-wave workgroup per CU can hold a 4-deep ring (152 KiB of LDS);
-    // smaller workgroups keep two slots so that several fit on a CU.
-    case 8: mla_decode_kernel<8, 4, kQkAhead, kPvAhead><<<grid, 8 * kWave, 0, stream>>>(a); break;
-    case 4: mla_decode_kernel<4, 2, kQkAhead, kPvAhead><<<grid, 4 * kWave, 0, stream>>>(a); break;
-    case 2: mla_decode_kernel<2, 2, kQkAhead, kPvAhead><<<grid, 2 * kWave, 0, stream>>>(a); break;
-    default: mla_decode_kernel<1, 2, kQkAhead, kPvAhead><<<grid, 1 * kWave, 0, stream>>>(a); break;
+  // Query rows go in launches of at most 65535 (the grid's z limit).
+  for (int32_t r0 = 0; r0 < a.rows; r0 += 65535) {
+    MlaArgs c = a;
+    c.row0 = r0;
+    const dim3 grid(a.max_np, tiles16 / nw, (unsigned)std::min<int32_t>(65535, a.rows - r0));
+    switch (nw) {
+      // One 8-wave workgroup per CU can hold a 4-deep ring (152 KiB of LDS);
+      // smaller workgroups keep two slots so that several fit on a CU.
+      case 8: mla_decode_kernel<8, 4, kQkAhead, kPvAhead><<<grid, 8 * kWave, 0, stream>>>(c); break;
+      case 4: mla_decode_kernel<4, 2, kQkAhead, kPvAhead><<<grid, 4 * kWave, 0, stream>>>(c); break;
+      case 2: mla_decode_kernel<2, 2, kQkAhead, kPvAhead><<<grid, 2 * kWave, 0, stream>>>(c); break;
+      default: mla_decode_kernel<1, 2, kQkAhead, kPvAhead><<<grid, 1 * kWave, 0, stream>>>(c); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace pkv

@@ -86,8 +86,8 @@ bool prefill_mfma_supported(int32_t dtype, int32_t head_dim);
 
 // MLA absorbed decode on MFMA (mla.hip); partials share the decode workspace layout.
 struct MlaArgs {
-  const void* q;       // [B, H, 512]
-  const void* q_rope;  // [B, H, 64]
+  const void* q;       // [rows, H, 512]
+  const void* q_rope;  // [rows, H, 64]
   const void* c_nope;  // [num_blocks, bs, 1, 512]
   const void* c_rope;  // [num_blocks, bs, 1, 64]
   const int32_t* block_table;
@@ -100,6 +100,9 @@ struct MlaArgs {
   float scale_log2e;
   int32_t out_dtype;
   int32_t waves_per_group;  // 16-head waves per workgroup (0 = up to 8)
+  const int32_t* cu_seqlens_q;  // prefill: [batch + 1] row offsets of the sequences; decode: null
+  int32_t rows;                 // query rows: batch (decode) or total_q (prefill)
+  int32_t row0;                 // first row of this launch (set by launch_mla_decode)
 };
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
 bool mla_decode_supported(int32_t dtype, int32_t head_dim, int32_t rope_dim, int32_t num_q_heads);

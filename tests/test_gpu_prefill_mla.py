@@ -160,3 +160,48 @@ def test_mla_full_size_sampled(orc):
     np.testing.assert_array_equal(host(slots), slots_ref)
     assert np.all(np.isfinite(as_f64(out)))
     assert_rows_close(out, ref, BF16_TOL, rows=units)
+
+
+# --------------------------------------------------------------------------- MLA absorbed prefill
+
+MLA_PREFILL_MATRIX = [
+    # B, H, bs, cached, new, window
+    (2, 16, 128, [5, 300], [7, 70], 0),
+    (3, 128, 64, [9, 1, 500], [3, 4, 2], 0),        # multi-token decode: 2-4 rows per sequence
+    (2, 32, 16, [100, 0], [40, 60], 0),
+    (2, 128, 128, [600, 90], [130, 200], 100),      # sliding window
+    (3, 48, 32, [0, 200, 17], [50, 0, 9], 0),       # 3 head tiles, a sequence with no new rows
+]
+
+
+@pytest.mark.parametrize("shape", MLA_PREFILL_MATRIX)
+def test_mla_prefill_matches_oracle(orc, shape):
+    B, H, bs, cached, new, w = shape
+    case = workloads.prefill_case(sum(cached) + H + w, B, H, 1, 512, "bf16", cached=cached, new=new,
+                                  block_size=bs, window=w, null_block=True, rope_dim=64,
+                                  scale=1.0 / np.sqrt(576.0))
+    ref, c_ref, slots_ref = oracle_run(orc, case)
+    d = DeviceCase(case)
+    out, slots = d.run()
+    np.testing.assert_array_equal(host(slots), slots_ref)
+    assert host(d.cache.k_cache).tobytes() == c_ref.k_cache.tobytes()
+    assert host(d.cache.k_rope_cache).tobytes() == c_ref.k_rope_cache.tobytes()
+    assert_rows_close(out, ref, BF16_TOL)
+    out32, _ = DeviceCase(case).run(out_dtype=torch.float32)
+    assert_rows_close(out32, ref, ACC_TOL)
+
+
+def test_mla_prefill_last_row_equals_decode(orc):
+    """The last new row of each sequence is the decode step at the full length."""
+    import paged_kv_cache_80_amd as pkv
+    case = workloads.prefill_case(11, 3, 32, 1, 512, "bf16", cached=[40, 300, 7], new=[3, 1, 25],
+                                  block_size=32, null_block=True, rope_dim=64)
+    d = DeviceCase(case)
+    out, _ = d.run(out_dtype=torch.float32)
+    cu = case.cu_seqlens_q
+    last = torch.from_numpy((cu[1:] - 1).astype(np.int64)).cuda()
+    q_last, qr_last = d.q[last].contiguous(), d.q_rope[last].contiguous()
+    dec = pkv.paged_attn_decode(q_last, d.cache, d.block_table, d.seq_lens, case.scale, q_rope=qr_last,
+                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(as_f64(dec), as_f64(out[last]), rtol=0, atol=1e-5)

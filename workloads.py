@@ -327,6 +327,21 @@ def mla_decode(seed: int = 0) -> Case:
                        scale=1.0 / math.sqrt(576.0), name="mla_decode")
 
 
+def mla_mtp_decode(seed: int = 0) -> Case:
+    """MLA absorbed multi-token decode: the mla_decode shapes (B=64, 128 heads,
+    latent 512 + rope 64, 8192 keys per sequence) with 4 new query rows per
+    sequence under the bottom-right causal mask (8188 cached + 4 new)."""
+    return prefill_case(seed, 64, 128, 1, 512, "bf16", cached=8188, new=4, max_blocks=64, rope_dim=64,
+                        scale=1.0 / math.sqrt(576.0), name="mla_mtp_decode")
+
+
+def mla_chunked_prefill(seed: int = 0) -> Case:
+    """MLA absorbed chunked prefill: B=4, 128 heads, latent 512 + rope 64,
+    4096 cached tokens plus 512 new query rows per sequence, causal."""
+    return prefill_case(seed, 4, 128, 1, 512, "bf16", cached=4096, new=512, max_blocks=36, rope_dim=64,
+                        scale=1.0 / math.sqrt(576.0), name="mla_chunked_prefill")
+
+
 WORKLOADS = {
     "tiny_f32_decode": tiny_f32_decode,
     "mha_decode_7b": mha_decode_7b,
@@ -334,4 +349,6 @@ WORKLOADS = {
     "gqa_decode_70b_window4096": lambda seed=0: gqa_decode_70b(seed, window=4096),
     "chunked_prefill": chunked_prefill,
     "mla_decode": mla_decode,
+    "mla_mtp_decode": mla_mtp_decode,
+    "mla_chunked_prefill": mla_chunked_prefill,
 }
