@@ -74,9 +74,23 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
   __shared__ __attribute__((aligned(16))) uint16_t r_lds[NBUF][kKeyTile][kR];
   __shared__ int32_t s_blk[kMaxBpp];
 
-  const int part = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int row = a.row0 + (int)blockIdx.z;  // query row: the sequence (decode) or a row of q (prefill)
+  int part = blockIdx.x;
+  int hg = blockIdx.y;
+  int zi = blockIdx.z;
+  if (a.cu_seqlens_q) {
+    // Prefill: workgroups are dealt to the 8 XCDs round robin by launch order.
+    // Renumber them so that each XCD takes a contiguous run of query rows --
+    // neighbouring rows of one sequence read the same latent tiles and then
+    // share that XCD's L2.  The grid is padded to a multiple of 8.
+    const int nwg = gridDim.x * gridDim.y * gridDim.z;
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int logical = (lin & 7) * (nwg >> 3) + (lin >> 3);
+    part = logical % gridDim.x;
+    hg = (logical / gridDim.x) % gridDim.y;
+    zi = logical / (gridDim.x * gridDim.y);
+    if (zi >= a.rows - a.row0) return;  // padding workgroup
+  }
+  const int row = a.row0 + zi;  // query row: the sequence (decode) or a row of q (prefill)
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -309,11 +323,18 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   // Up to 8 waves (128 heads) per workgroup; the head groups tile H exactly.
   int nw = a.waves_per_group > 0 ? a.waves_per_group : 8;
   while (tiles16 % nw) nw >>= 1;
-  // Query rows go in launches of at most 65535 (the grid's z limit).
-  for (int32_t r0 = 0; r0 < a.rows; r0 += 65535) {
+  // Query rows go in launches of at most 65528 (the grid's z limit, rounded
+  // down to a multiple of 8); prefill pads each launch to a multiple of 8
+  // workgroups for the XCD renumbering (extra rows exit at once).
+  for (int32_t r0 = 0; r0 < a.rows; r0 += 65528) {
     MlaArgs c = a;
     c.row0 = r0;
-    const dim3 grid(a.max_np, tiles16 / nw, (unsigned)std::min<int32_t>(65535, a.rows - r0));
+    int32_t nz = std::min<int32_t>(65528, a.rows - r0);
+    if (a.cu_seqlens_q) {
+      const int64_t per_z = (int64_t)a.max_np * (tiles16 / nw);
+      while ((per_z * nz) % 8) ++nz;
+    }
+    const dim3 grid(a.max_np, tiles16 / nw, (unsigned)nz);
     switch (nw) {
       // One 8-wave workgroup per CU can hold a 4-deep ring (152 KiB of LDS);
       // smaller workgroups keep two slots so that several fit on a CU.
