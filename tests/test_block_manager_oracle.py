@@ -1,0 +1,218 @@
+"""Pins for the block-manager oracle (oracle/block_manager.py), CPU only.
+
+What fixes the oracle here is the design page's stated behaviour (null block taken
+first, FIFO issue, double-free detection, all-or-nothing allocation, window skip
+count), the skill page's worked slot example, and invariants that hold for any
+schedule -- block conservation, exclusive ownership, table length, the null entries
+of a sliding window -- plus the sizing formulas checked against what a schedule
+actually needs, not against a retyped formula.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import block_manager as bm
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def test_null_block_is_first_and_never_issued():
+    pool = bm.BlockPool(8)
+    assert pool.null_block == 0
+    assert pool.get_new_blocks(7) == [1, 2, 3, 4, 5, 6, 7]
+    with pytest.raises(bm.AllocError):
+        pool.get_new_blocks(1)
+
+
+def test_fifo_issue_and_tail_reuse():
+    pool = bm.BlockPool(8)
+    assert pool.get_new_blocks(3) == [1, 2, 3]
+    pool.free_blocks([2])
+    pool.free_blocks([1])
+    assert pool.get_new_blocks(6) == [4, 5, 6, 7, 2, 1]
+
+
+@pytest.mark.parametrize("bad", [[3, 3], [0], [5], [9], [-1]])
+def test_bad_free_is_rejected_and_changes_nothing(bad):
+    pool = bm.BlockPool(8)
+    pool.get_new_blocks(4)  # 1..4 held, 5..7 free
+    before = (list(pool.free_queue), set(pool.free_set))
+    with pytest.raises(bm.AllocError):
+        pool.free_blocks(bad)
+    assert (list(pool.free_queue), set(pool.free_set)) == before
+
+
+def test_window_skip_count():
+    m = bm.SingleTypeManager(bm.SLIDING, 16, 4, 1000, sliding_window=10)
+    # with c computed tokens the next query (position c) sees c-9..c: c-9 tokens skipped
+    assert [m.num_skipped_tokens(c) for c in (0, 5, 9, 10, 11, 30)] == [0, 0, 0, 1, 2, 21]
+    f = bm.SingleTypeManager(bm.FULL, 16, 4, 1000)
+    assert f.num_skipped_tokens(10 ** 6) == 0
+
+
+def test_slot_mapping_worked_example():
+    gold = json.load(open(os.path.join(HERE, "golden", "slot_examples.json")))
+    lay, ex = gold["layout"], gold["mapping_example"]
+    table = np.arange(lay["total_blocks"]).reshape(lay["batch_size"], -1).tolist()
+    assert bm.prepare_slot_mapping(table, lay["block_size"], [ex["batch_idx"]], [ex["seq_pos"]]) == [ex["slot"]]
+    d = gold["decode_example"]  # the decode token of a sequence holding kv_len tokens sits at position kv_len
+    assert bm.prepare_slot_mapping(table, lay["block_size"], [0, 1], d["kv_len"]) == d["slot_mapping"]
+
+
+def test_format_usage_matches_the_pages_form():
+    kvm = bm.KVCacheManager([(bm.FULL, 100, 0), (bm.SLIDING, 100, 64)], block_size=16, max_model_len=4096)
+    assert kvm.allocate_slots("a", 0, 12 * 16)
+    # the window keeps every block of a fresh prefill (nothing computed before it)
+    assert kvm.format_usage() == "full:12/100,sliding:12/100"
+    kvm.free("a")
+    assert kvm.format_usage() == "full:0/100,sliding:0/100"
+
+
+def _held(m):
+    return [b for blocks in m.req_to_blocks.values() for b in blocks if b != m.null_block]
+
+
+def _check_invariants(kvm):
+    for m in kvm.managers:
+        held = _held(m)
+        assert len(held) == len(set(held)), "a block is held twice"
+        assert not set(held) & m.pool.free_set
+        assert len(held) + m.pool.num_free() + 1 == m.pool.num_blocks
+        for blocks in m.req_to_blocks.values():  # null entries only before real ones
+            real = [b != m.null_block for b in blocks]
+            assert real == sorted(real)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_schedules_keep_the_invariants(seed):
+    rng = np.random.default_rng(seed)
+    kvm = bm.KVCacheManager([(bm.FULL, 60, 0), (bm.SLIDING, 40, 37)], block_size=8, max_model_len=300)
+    computed = {}
+    for _ in range(400):
+        if rng.integers(0, 10) == 0 and computed:
+            r = list(computed)[rng.integers(0, len(computed))]
+            kvm.free(r)
+            del computed[r]
+            assert all(r not in m.req_to_blocks for m in kvm.managers)
+            _check_invariants(kvm)
+            continue
+        r = int(rng.integers(0, 6))
+        c = computed.get(r, 0)
+        new = int(rng.integers(1, 40)) if c == 0 else int(rng.integers(1, 4))
+        look = int(rng.integers(0, 3))
+        before = [{k: len(v) for k, v in m.req_to_blocks.items()} for m in kvm.managers]
+        if kvm.allocate_slots(r, c, new, look):
+            need = min(c + new + look, kvm.max_model_len)
+            for m in kvm.managers:
+                blocks = m.req_to_blocks[r]
+                assert len(blocks) == max(before[kvm.managers.index(m)].get(r, 0), math.ceil(need / m.block_size))
+                skipped = m.num_skipped_tokens(min(c, kvm.max_model_len)) // m.block_size
+                assert all(b == m.null_block for b in blocks[:skipped])
+                assert all(b != m.null_block for b in blocks[skipped:])
+            computed[r] = min(c + new, kvm.max_model_len)
+        else:  # all or nothing: no table grew, no table appeared
+            for i, m in enumerate(kvm.managers):
+                assert {k: len(v) for k, v in m.req_to_blocks.items()} == before[i]
+        _check_invariants(kvm)
+
+
+def test_shortfall_allocates_nothing_anywhere():
+    kvm = bm.KVCacheManager([(bm.FULL, 50, 0), (bm.SLIDING, 4, 16)], block_size=8, max_model_len=1000)
+    assert kvm.allocate_slots("a", 0, 24)   # 3 blocks each
+    assert not kvm.allocate_slots("b", 0, 16)  # the window pool has 0 free, 2 needed
+    assert "b" not in kvm.managers[0].req_to_blocks or kvm.managers[0].req_to_blocks["b"] == []
+    assert kvm.managers[0].pool.num_free() == 49 - 3
+
+
+def _decode_schedule(kvm, conc, steps, lookahead):
+    """conc requests advancing one token a step from a one-token prompt; returns False
+    at the first allocation that fails."""
+    computed = {r: 0 for r in range(conc)}
+    for r in range(conc):
+        if not kvm.allocate_slots(r, 0, 1, lookahead):
+            return False
+        computed[r] = 1
+    for _ in range(steps):
+        for r in range(conc):
+            if not kvm.allocate_slots(r, computed[r], 1, lookahead):
+                return False
+            computed[r] += 1
+    return True
+
+
+@pytest.mark.parametrize("window,next_n,bs", [(40, 0, 8), (37, 1, 8), (64, 2, 16), (5, 0, 4)])
+def test_fixed_block_num_covers_a_window_schedule_and_is_tight(window, next_n, bs):
+    conc, steps = 3, 6 * window
+    n = bm.calculate_block_num_fixed(conc, window, next_n, bs)
+    ok = bm.KVCacheManager([(bm.SLIDING, n, window)], bs, 10 ** 6)
+    assert _decode_schedule(ok, conc, steps, 2 * next_n)
+    # T = W + 2 next_n consecutive tokens touch at most ceil((T - 1) / bs) + 1 blocks;
+    # requests in lockstep all reach that together, so one block per request less fails
+    peak = math.ceil((window + 2 * next_n - 1) / bs) + 1
+    assert n >= conc * peak + 1
+    small = bm.KVCacheManager([(bm.SLIDING, conc * (peak - 1) + 1, window)], bs, 10 ** 6)
+    assert not _decode_schedule(small, conc, steps, 2 * next_n)
+    exact = bm.KVCacheManager([(bm.SLIDING, conc * peak + 1, window)], bs, 10 ** 6)
+    assert _decode_schedule(exact, conc, steps, 2 * next_n)
+
+
+@pytest.mark.parametrize("max_len,conc,bs", [(100, 3, 8), (64, 2, 16), (1, 1, 128)])
+def test_full_block_num_fits_exactly_max_length_requests(max_len, conc, bs):
+    n = bm.calculate_block_num_full(max_len, conc, bs)
+    kvm = bm.KVCacheManager([(bm.FULL, n, 0)], bs, max_len)
+    assert all(kvm.allocate_slots(r, 0, max_len) for r in range(conc))
+    assert kvm.managers[0].pool.num_free() == 0
+    tight = bm.KVCacheManager([(bm.FULL, n - 1, 0)], bs, max_len)
+    assert not all(tight.allocate_slots(r, 0, max_len) for r in range(conc))
+
+
+def test_budget_block_num():
+    # 1 MB after 200 KB of window blocks, 1000 bytes a token: 800 tokens -> 50 blocks of 16 + null
+    assert bm.calculate_block_num_budget(1_000_000, 200_000, 1000, 16) == 51
+    assert bm.calculate_block_num_budget(100, 200, 10, 16) == 1  # nothing left: the null block only
+
+
+def test_block_table_rows_are_padded_with_the_null_block():
+    kvm = bm.KVCacheManager([(bm.FULL, 20, 0)], 4, 100)
+    kvm.allocate_slots("x", 0, 9)
+    kvm.allocate_slots("y", 0, 2)
+    t = kvm.prepare_block_table(0, ["x", "y"], 5)
+    assert t == [[1, 2, 3, 0, 0], [4, 0, 0, 0, 0]]
+    with pytest.raises(bm.AllocError):
+        kvm.prepare_block_table(0, ["x"], 2)
+
+
+@pytest.mark.parametrize("fill", [np.nan, 1e30])
+def test_window_tables_give_attention_over_the_last_window(orc, fill):
+    """Decode steps through a sliding-window manager: its tables (null entries before
+    the window) with the attention oracle equal attention over a contiguous cache
+    holding only the last W tokens -- the window semantics of the kernels."""
+    rng = np.random.default_rng(3)
+    bs, W, D, steps = 4, 9, 8, 30
+    kvm = bm.KVCacheManager([(bm.SLIDING, 12, W)], bs, 1000)
+    m = kvm.managers[0]
+    k_cache = np.full((12, bs, 1, D), fill, dtype=np.float32)
+    v_cache = np.full((12, bs, 1, D), fill, dtype=np.float32)
+    ks, vs = [], []
+    for c in range(steps):
+        assert kvm.allocate_slots("r", c, 1)
+        k, v = rng.standard_normal((2, D)).astype(np.float32)
+        ks.append(k)
+        vs.append(v)
+        table = kvm.prepare_block_table(0, ["r"], 1000 // bs)
+        slot = bm.prepare_slot_mapping(table, bs, [0], [c])[0]
+        assert slot // bs != m.null_block
+        k_cache.reshape(-1, 1, D)[slot, 0] = k
+        v_cache.reshape(-1, 1, D)[slot, 0] = v
+        q = rng.standard_normal((1, 1, D)).astype(np.float32)
+        bt = np.asarray(table, dtype=np.int32)
+        got = orc.paged_decode(q, k_cache, v_cache, bt, np.array([c + 1], np.int32), 0.5, window=W)
+        lo = max(0, c + 1 - W)
+        s = (np.asarray(ks[lo:], np.float64) @ q[0, 0].astype(np.float64)) * 0.5
+        p = np.exp(s - s.max())
+        want = (p / p.sum()) @ np.asarray(vs[lo:], np.float64)
+        np.testing.assert_allclose(got[0, 0], want, rtol=1e-12, atol=1e-12)
+    assert len(_held(m)) <= math.ceil(W / bs) + 1
