@@ -26,7 +26,13 @@ native allocator):
     already computed before a step (the quantity allocate_slots hands to
     remove_skipped_blocks): with c computed tokens a sliding window W skips
     max(0, c - W + 1) tokens, and table entries wholly inside them hold the null
-    block.  A fresh prefill (c = 0) therefore gets real blocks only.
+    block.  A fresh prefill (c = 0) therefore gets real blocks for all its tokens,
+    and they go back to the pool as the window moves.  The page has a prefill take
+    real blocks for the window only; that presumes attention over the step's own
+    keys outside the cache, while here every query of a step reads its keys from the
+    cache, so each new token needs a real block during its step.  The sizing of
+    section 4.2.1 then covers the decode steady state; a pool must also hold the
+    longest prompt chunk.
   * remove_skipped_blocks walks the skipped entries from the last one backwards,
     stops at the first null entry (earlier ones were nulled before) and returns the
     blocks to the pool in that order.

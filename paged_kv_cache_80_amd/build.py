@@ -2,8 +2,9 @@
 
     python -m paged_kv_cache_80_amd.build
 
-Each .hip source compiles to an object under _build/ in parallel, then one
-link step writes paged_kv_cache_80_amd/libpkv.so.
+Each .hip source (hipcc, gfx950) and each host-only .cpp source (g++) compiles to
+an object under _build/ in parallel, then one link step writes
+paged_kv_cache_80_amd/libpkv.so.
 """
 from __future__ import annotations
 
@@ -31,9 +32,16 @@ COMMON = [
 ]
 
 
+HOST_CXX = os.environ.get("CXX", "g++")
+HOST = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):  # host-only C++ (the block allocator)
+        cmd = [HOST_CXX, *HOST, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -42,7 +50,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "device_common.h"
+#include "pkv_error.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -447,3 +448,8 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
 }
 
 }  // extern "C"
+
+namespace pkv {
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+void clear_last_error() { g_last_error.clear(); }
+}  // namespace pkv

@@ -1,7 +1,8 @@
-"""The C-ABI library loads and exports every symbol include/pkv.h declares; host-side
+"""The C-ABI library loads and exports every symbol include/*.h declares; host-side
 argument checks reject malformed calls before anything is launched (no GPU needed:
 no call here reaches a kernel launch)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,15 +11,16 @@ import pytest
 import paged_kv_cache_80_amd as pkv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pkv.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?(?:pkv_status|size_t|const char\*|char\*)\s*\**\s*(\w+)\s*\(",
-                       src, flags=re.M)
-    return set(names)
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?(?:pkv_status|size_t|void|const char\*|char\*)\s*\**\s*(\w+)\s*\(",
+                                src, flags=re.M))
+    return names
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +32,8 @@ def lib():
 
 
 def test_header_declares_the_documented_entry_points():
-    assert _declared() == set(pkv.EXPORTS)
+    from paged_kv_cache_80_amd import blocks
+    assert _declared() == set(pkv.EXPORTS) | set(blocks.EXPORTS)
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -311,3 +311,60 @@ def test_mha_decode_7b_full_size(orc):
 def test_gqa_decode_70b_full_size(orc, window):
     """llama2-70B layer: B=32, H=64/8, ragged 1K-32K, null block 0 (NaN-filled)."""
     _full_size_check(orc, workloads.gqa_decode_70b(0, window=window))
+
+
+# --------------------------------------------------------------------------- tables from the allocator
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_over_allocator_window_tables(orc, dtype):
+    """Decode with the tables the native block allocator keeps for a sliding-window
+    group: entries before each window hold the NaN-filled null block, the kernels and
+    the oracle agree, and slots resolved on the GPU match the allocator's mapping."""
+    import paged_kv_cache_80_amd as pkv
+    from paged_kv_cache_80_amd import blocks
+    from oracle import block_manager as bm
+    rng = np.random.default_rng(5)
+    B, H, Hkv, D, bs, W = 5, 16, 4, 128, 16, 200
+    # a step's new tokens all take real blocks (this step's attention reads them from
+    # the cache), so the pool holds the longest prompt of every request, then windows
+    prompt = rng.integers(20, 600, size=B)
+    nblocks = B * (-(-600 // bs) + 1) + 1
+    kvm = blocks.KVCacheManager([(blocks.ATTN_SLIDING, nblocks, W)], bs, 4096)
+    computed = [0] * B
+    for r in range(B):
+        assert kvm.allocate_slots(r, 0, int(prompt[r]))
+        computed[r] = int(prompt[r])
+    for _ in range(int(rng.integers(30, 90))):  # decode steps, one token each
+        for r in range(B):
+            assert kvm.allocate_slots(r, computed[r], 1)
+            computed[r] += 1
+    lens = np.array(computed, dtype=np.int32)
+    mb = int(-(-lens.max() // bs))
+    table = kvm.prepare_block_table(0, list(range(B)), mb)
+    assert (table[:, 0] == 0).any()  # some window has moved past its first block
+    assert kvm.num_free_blocks(0) >= nblocks - 1 - B * (-(-W // bs) + 1)  # prompts' blocks went back
+    # every position in a window lives in a real block; real blocks hold finite data
+    # (rows before a window inside its first block are stale, not garbage), the null
+    # block NaN
+    k_cache = rng.standard_normal((nblocks, bs, Hkv, D)).astype(np.float32)
+    v_cache = rng.standard_normal((nblocks, bs, Hkv, D)).astype(np.float32)
+    k_cache[0] = np.nan
+    v_cache[0] = np.nan
+    if dtype == "bf16":
+        k_cache, v_cache = workloads.bf16_bits(k_cache), workloads.bf16_bits(v_cache)
+    for b in range(B):
+        assert all(table[b, p // bs] != 0 for p in range(max(0, lens[b] - W), lens[b]))
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    if dtype == "bf16":
+        q = workloads.bf16_bits(q)
+    scale = 1.0 / np.sqrt(D)
+    ref = orc.paged_decode(q, k_cache, v_cache, table, lens, scale, window=W)
+    cache = pkv.PagedKVCache(dev(k_cache), dev(v_cache), None)
+    out = pkv.paged_attn_decode(dev(q), cache, dev(table), dev(lens), scale, W)
+    torch.cuda.synchronize()
+    assert_rows_close(out, ref, F32_TOL if dtype == "f32" else BF16_TOL)
+    pos = (lens - 1).astype(np.int32)
+    slots = pkv.pkv_resolve_slots(dev(table), bs, dev(np.arange(B, dtype=np.int32)), dev(pos))
+    torch.cuda.synchronize()
+    want = bm.prepare_slot_mapping(table.tolist(), bs, list(range(B)), pos.tolist())
+    assert host(slots).tolist() == want
