@@ -115,6 +115,7 @@ PROFILED = {
     "mla_decode": ("mla_decode_mla_decode.md", [_CSRC + "mla.hip", _CSRC + "decode.hip"] + _COMMON),
     "mla_mtp_decode": ("mla_decode_mla_mtp_decode.md", [_CSRC + "mla.hip"] + _COMMON),
     "mla_chunked_prefill": ("mla_decode_mla_chunked_prefill.md", [_CSRC + "mla.hip"] + _COMMON),
+    "mla_latent_write": ("latent_write_mla_latent_write.md", [_CSRC + "latent_write.hip"] + _COMMON),
 }
 
 
@@ -204,6 +205,111 @@ def cpu_baseline(case, target_s):
             "sample": f"{sample}, fp64, {threads} threads", "ms_per_step": round(el * 1e3, 3)}
 
 
+def latent_bytes(case):
+    """Bytes the fused latent write must move per step, by call: (resolve, fused write)."""
+    eb = 2 if case.dtype == "bf16" else 4
+    T = case.T
+    resolve = T * 16
+    row, rope = (512 + 64) * eb, 64 * eb
+    write = T * (row + 2 * rope + 4 + row * (2 if case.outputs else 1)) + 512 * eb
+    return resolve, write
+
+
+def cpu_baseline_latent(case, target_s):
+    """The latent-write oracle on the host cores: whole steps (slots + RMSNorm + RoPE + write of
+    every token), repeated to about the time target."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from helpers import oracle_latent
+
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle_latent(oracle, case)
+    one = time.perf_counter() - t0
+    reps = max(1, int(target_s / max(one, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle_latent(oracle, case)
+    el = (time.perf_counter() - t0) / reps
+    r, w = latent_bytes(case)
+    return {"value": round((r + w) / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole steps of {case.name} seed {case.seed_label} ({case.T} tokens), fp64 numpy, "
+                      f"{el * 1e3:.1f} ms per step, 1 thread", "ms_per_step": round(el * 1e3, 3)}
+
+
+def run_latent(args, case, torch, pkv):
+    """One step = resolve the new tokens' slots, then the fused RMSNorm + RoPE + cache write."""
+    dev = lambda a: _dev(torch, a)  # noqa: E731
+    cache = pkv.PagedKVCache(dev(case.cache_nope), None, dev(case.cache_rope))
+    bt, bidx, pos = dev(case.block_table), dev(case.new_batch_idx), dev(case.new_pos)
+    lat, gamma, cos, sin = dev(case.latent), dev(case.gamma), dev(case.cos), dev(case.sin)
+    slots = torch.empty(case.T, dtype=torch.int32, device="cuda")
+    tdt = lat.dtype
+    kn = torch.empty((case.T, 512), dtype=tdt, device="cuda") if case.outputs else None
+    kr = torch.empty((case.T, 64), dtype=tdt, device="cuda") if case.outputs else None
+
+    def step(e0=None, e1=None):
+        pkv.pkv_resolve_slots(bt, case.block_size, bidx, pos, slots_out=slots)
+        if e0 is not None:
+            e0.record()
+        pkv.kv_rmsnorm_rope_cache(lat, gamma, cos, sin, slots, case.eps, cache, rope_layout=case.layout,
+                                  k_nope_out=kn, k_rope_out=kr)
+        if e1 is not None:
+            e1.record()
+
+    ms_step, ms_k = _timed(torch, step, args)
+    r_b, w_b = latent_bytes(case)
+    value = (r_b + w_b) / (ms_step * 1e-3) / 1e9
+    k_gbs = w_b / (ms_k * 1e-3) / 1e9
+    result = _result(args, case, value, ms_step, {"workload": case.name, "batch": case.B, "tokens": case.T,
+                                                  "latent_dim": 512, "rope_dim": 64, "block_size": case.block_size,
+                                                  "rope_layout": "half" if case.layout == 0 else "interleaved",
+                                                  "returned_rows": case.outputs, "seed": args.seed})
+    result.update({"hbm_frac": round(value / HBM_PEAK_GBS, 4), "tokens_per_s": round(case.T / (ms_step * 1e-3), 1),
+                   "kernel_ms": round(ms_k, 4), "kernel_GBps": round(k_gbs, 2)})
+    result["roofline"] = {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(args.workload),
+                          "kernel": "kv_rmsnorm_rope_cache", "bytes_per_launch": w_b}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_latent(case, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def _timed(torch, step, args):
+    """W untimed steps, then K timed steps between synchronisations; returns (ms per step,
+    mean ms between each step's two events)."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for e0, e1 in ev:
+        step(e0, e1)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / args.steps, float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
+def _result(args, case, value, ms_step, config):
+    return {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": config,
+    }
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -226,6 +332,9 @@ def main():
 
     case = workloads.WORKLOADS[args.workload](args.seed)
     case.seed_label = args.seed
+    if case.kind == "latent_write":
+        run_latent(args, case, torch, pkv)
+        return
     dev = lambda a: _dev(torch, a)  # noqa: E731
     cache = pkv.PagedKVCache(dev(case.k_cache), dev(case.v_cache), dev(case.k_rope_cache))
     bt, sl = dev(case.block_table), dev(case.seq_lens)
@@ -261,19 +370,7 @@ def main():
         if e1 is not None:
             e1.record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for e0, e1 in ev:
-        step(e0, e1)
-    end.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
-    ms_attn = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    ms_step, ms_attn = _timed(torch, step, args)
 
     r_b, w_b, a_b, kv_b = algorithmic_bytes(case)
     flops = algorithmic_flops(case)
@@ -290,29 +387,18 @@ def main():
                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
     roofline.update({"traffic": profiled_traffic(args.workload), "kernel": kernel, "bytes_per_launch": a_b,
                      "flops_per_launch": flops})
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": case.dtype,
-        "data": "synthetic",
-        "config": {"workload": case.name, "batch": case.B, "num_q_heads": case.H, "num_kv_heads": case.Hkv,
-                   "head_dim": case.D, "rope_dim": case.rope_dim, "block_size": case.block_size,
-                   "window": case.window, "seq_len_total": int(case.seq_lens.sum()), "seed": args.seed},
+    result = _result(args, case, value, ms_step,
+                     {"workload": case.name, "batch": case.B, "num_q_heads": case.H, "num_kv_heads": case.Hkv,
+                      "head_dim": case.D, "rope_dim": case.rope_dim, "block_size": case.block_size,
+                      "window": case.window, "seq_len_total": int(case.seq_lens.sum()), "seed": args.seed})
+    result.update({
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(case.new_pos.size / (ms_step * 1e-3), 1),
         "attention_ms": round(ms_attn, 4),
         "attention_GBps": round(attn_gbs, 2),
         "mfma_util": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roofline,
-    }
+    })
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -105,6 +105,37 @@ pkv_status kv_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const
                           const void* v, const void* k_rope, const pkv_paged_cache* cache,
                           void* stream);
 
+typedef enum {
+  PKV_ROPE_HALF = 0,       /* element i pairs with i + rope_dim/2 (the first half with the second) */
+  PKV_ROPE_INTERLEAVED = 1 /* elements 2k and 2k+1 form a pair                                  */
+} pkv_rope_layout;
+
+/* Fused RMSNorm + RoPE + cache write of the MLA latent ("Ascend NPU
+ * standalone-deployment KVCache guide", MLA section: the single fused step that
+ * normalises, rotates and writes the latent and can also return the rows; the
+ * "KVCache optimisation skill" page lists it as the slot_mapping-driven fused
+ * writer).  For each token t < num_tokens, with latent row t = [c | k_pe]
+ * (c: head_dim = 512 values, k_pe: rope_dim = 64 values):
+ *     nope = c / sqrt(mean(c * c) + eps) * gamma                    (fp32 arithmetic)
+ *     rope[i] = k_pe[i] * cos[t][i] -/+ k_pe[j] * sin[t][i]          (j: i's pair partner;
+ *               minus for the first element of the pair, plus for the second)
+ *     cache->k_cache row slot_mapping[t] = nope, cache->k_rope_cache row = rope
+ *     (a negative slot writes nothing), and k_nope_out[t] = nope, k_rope_out[t] = rope
+ *     when the outputs are given.
+ *   cache        : an MLA cache (latent 512, rope 64, one head, v_cache == k_cache), f32 or bf16
+ *   latent       : [num_tokens, 512 + 64]; gamma: [512]; cos, sin: [num_tokens, 64], the
+ *                  values at each token's position; all in cache->dtype
+ *   rope_layout  : pkv_rope_layout
+ *   eps          : finite, >= 0
+ *   k_nope_out   : [num_tokens, 512] and k_rope_out [num_tokens, 64] in cache->dtype, both or
+ *                  neither (NULL)
+ *   slot_mapping : [num_tokens]; slots must be distinct.
+ * The outputs and the cache must not overlap the inputs. */
+pkv_status kv_rmsnorm_rope_cache(const void* latent, const void* gamma, const void* cos, const void* sin,
+                                 const int32_t* slot_mapping, int32_t num_tokens, float eps,
+                                 int32_t rope_layout, const pkv_paged_cache* cache, void* k_nope_out,
+                                 void* k_rope_out, void* stream);
+
 /* Bytes of workspace paged_attn_decode needs for these arguments (0 is possible). */
 size_t paged_attn_decode_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache);
 

@@ -7,7 +7,8 @@ the GPU, pass their device pointers and the current HIP stream, and raise
 missing, ``load()`` raises.
 
 Names follow the C ABI: ``pkv_resolve_slots``, ``kv_cache_write``,
-``paged_attn_decode``, ``paged_attn_prefill`` (+ their ``*_workspace`` sizes).
+``kv_rmsnorm_rope_cache``, ``paged_attn_decode``, ``paged_attn_prefill`` (+ their
+``*_workspace`` sizes).
 """
 from __future__ import annotations
 
@@ -22,12 +23,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_F32, PKV_BF16 = 0, 1
+PKV_ROPE_HALF, PKV_ROPE_INTERLEAVED = 0, 1
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED", 3: "PKV_ERR_WORKSPACE",
           4: "PKV_ERR_HIP"}
 
 # Every symbol include/pkv.h declares.
-EXPORTS = ("pkv_resolve_slots", "kv_cache_write", "paged_attn_decode_workspace", "paged_attn_decode",
-           "paged_attn_prefill_workspace", "paged_attn_prefill", "pkv_last_error", "pkv_version")
+EXPORTS = ("pkv_resolve_slots", "kv_cache_write", "kv_rmsnorm_rope_cache", "paged_attn_decode_workspace",
+           "paged_attn_decode", "paged_attn_prefill_workspace", "paged_attn_prefill", "pkv_last_error",
+           "pkv_version")
 
 
 class PkvError(RuntimeError):
@@ -66,13 +69,15 @@ def load(path: str = LIB_PATH):
     pc, pp = ctypes.POINTER(PagedCacheDesc), ctypes.POINTER(AttnParams)
     lib.pkv_resolve_slots.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
     lib.kv_cache_write.argtypes = [P, i32, P, P, P, pc, P]
+    lib.kv_rmsnorm_rope_cache.argtypes = [P, P, P, P, P, i32, ctypes.c_float, i32, pc, P, P, P]
     lib.paged_attn_decode_workspace.argtypes = [pp, pc]
     lib.paged_attn_decode_workspace.restype = sz
     lib.paged_attn_decode.argtypes = [P, P, pc, P, P, pp, P, P, sz, P]
     lib.paged_attn_prefill_workspace.argtypes = [pp, pc, i32]
     lib.paged_attn_prefill_workspace.restype = sz
     lib.paged_attn_prefill.argtypes = [P, P, pc, P, P, P, i32, i32, pp, P, P, sz, P]
-    for f in (lib.pkv_resolve_slots, lib.kv_cache_write, lib.paged_attn_decode, lib.paged_attn_prefill):
+    for f in (lib.pkv_resolve_slots, lib.kv_cache_write, lib.kv_rmsnorm_rope_cache, lib.paged_attn_decode,
+              lib.paged_attn_prefill):
         f.restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
@@ -156,6 +161,24 @@ def kv_cache_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: Optional[torc
     d = cache.desc()
     _check(load().kv_cache_write(_ptr(_i32(slot_mapping)), slot_mapping.numel(), _ptr(k), _ptr(v),
                                  _ptr(k_rope), ctypes.byref(d), _stream(stream)))
+
+
+def kv_rmsnorm_rope_cache(latent: torch.Tensor, gamma: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+                          slot_mapping: torch.Tensor, eps: float, cache: PagedKVCache,
+                          rope_layout: int = PKV_ROPE_HALF, k_nope_out: Optional[torch.Tensor] = None,
+                          k_rope_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """RMSNorm(latent[:, :512]) * gamma and RoPE(latent[:, 512:]; cos, sin) into the MLA cache rows
+    slot_mapping[t] (negative slots skip), and into k_nope_out / k_rope_out when given."""
+    d = cache.desc()
+    n = slot_mapping.numel()
+    if latent.shape[0] != n or cos.shape[0] != n or sin.shape[0] != n:
+        raise ValueError("latent, cos, sin and slot_mapping must have one row per token")
+    for t in (latent, gamma, cos, sin, k_nope_out, k_rope_out):
+        if t is not None and t.dtype != cache.k_cache.dtype:
+            raise TypeError("every array must have the cache dtype")
+    _check(load().kv_rmsnorm_rope_cache(_ptr(latent), _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(_i32(slot_mapping)), n,
+                                        float(eps), rope_layout, ctypes.byref(d), _ptr(k_nope_out), _ptr(k_rope_out),
+                                        _stream(stream)))
 
 
 def _params(batch, num_q_heads, block_table, scale, window, out_dtype, split_tokens) -> AttnParams:

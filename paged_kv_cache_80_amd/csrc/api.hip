@@ -251,6 +251,41 @@ pkv_status kv_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const
                   "kv_cache_write launch");
 }
 
+pkv_status kv_rmsnorm_rope_cache(const void* latent, const void* gamma, const void* cos, const void* sin,
+                                 const int32_t* slot_mapping, int32_t num_tokens, float eps,
+                                 int32_t rope_layout, const pkv_paged_cache* cache, void* k_nope_out,
+                                 void* k_rope_out, void* stream) {
+  pkv_status s = check_cache(cache);
+  if (s) return s;
+  if (!is_mla(cache)) return fail(PKV_ERR_INVALID_ARG, "kv_rmsnorm_rope_cache needs an MLA cache (rope_dim > 0)");
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %d must be >= 0", num_tokens);
+  if (!(std::isfinite(eps) && eps >= 0.0f)) return fail(PKV_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (rope_layout != PKV_ROPE_HALF && rope_layout != PKV_ROPE_INTERLEAVED)
+    return fail(PKV_ERR_INVALID_ARG, "rope_layout %d is not PKV_ROPE_HALF or PKV_ROPE_INTERLEAVED", rope_layout);
+  if ((k_nope_out != nullptr) != (k_rope_out != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_nope_out and k_rope_out must be given together or not at all");
+  if (num_tokens == 0) return ok();
+  if (!latent || !gamma || !cos || !sin || !slot_mapping) return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned16(latent) || !aligned16(gamma) || !aligned16(cos) || !aligned16(sin) ||
+      (k_nope_out && (!aligned16(k_nope_out) || !aligned16(k_rope_out))))
+    return fail(PKV_ERR_INVALID_ARG, "latent / gamma / cos / sin / outputs must be 16-byte aligned");
+  pkv::LatentWriteArgs a{};
+  a.latent = latent;
+  a.gamma = gamma;
+  a.cos = cos;
+  a.sin = sin;
+  a.slot_mapping = slot_mapping;
+  a.cache_nope = cache->k_cache;
+  a.cache_rope = cache->k_rope_cache;
+  a.out_nope = k_nope_out;
+  a.out_rope = k_rope_out;
+  a.num_tokens = num_tokens;
+  a.eps = eps;
+  a.bf16 = cache->dtype == PKV_BF16;
+  a.interleaved = rope_layout == PKV_ROPE_INTERLEAVED;
+  return from_hip(pkv::launch_latent_write(a, static_cast<hipStream_t>(stream)), "kv_rmsnorm_rope_cache launch");
+}
+
 size_t paged_attn_decode_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache) {
   if (check_cache(cache) || check_params(params, cache)) return 0;
   return plan_decode(params, cache).ws_bytes;

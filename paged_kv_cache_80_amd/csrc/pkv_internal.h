@@ -24,6 +24,25 @@ struct WriteRows {
 hipError_t launch_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const WriteRows& rows,
                               hipStream_t stream);
 
+// Fused RMSNorm + RoPE + cache write of the MLA latent (latent_write.hip).
+// Latent width 512, rotary width 64, one latent head; every array in one dtype.
+struct LatentWriteArgs {
+  const void* latent;           // [num_tokens, 512 + 64]
+  const void* gamma;            // [512]
+  const void* cos;              // [num_tokens, 64]
+  const void* sin;              // [num_tokens, 64]
+  const int32_t* slot_mapping;  // [num_tokens]; negative: no cache write
+  void* cache_nope;             // [slots, 512]
+  void* cache_rope;             // [slots, 64]
+  void* out_nope;               // [num_tokens, 512] or NULL (then out_rope is NULL too)
+  void* out_rope;               // [num_tokens, 64]
+  int64_t num_tokens;
+  float eps;
+  int32_t bf16;
+  int32_t interleaved;
+};
+hipError_t launch_latent_write(const LatentWriteArgs& a, hipStream_t stream);
+
 // Split-K decode on the vector ALUs (decode.hip).
 struct DecodeArgs {
   const void* q;

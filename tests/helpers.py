@@ -63,3 +63,24 @@ def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     num = np.linalg.norm(got - ref, axis=-1)
     den = np.linalg.norm(ref, axis=-1)
     return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values or bfloat16 raw bits -> float64 (exact)."""
+    return (a if dtype == "f32" else workloads.bf16_to_f32(a)).astype(np.float64)
+
+
+def oracle_latent(orc, case, tokens=None):
+    """Expected results of a workloads.LatentCase from the oracle: (slots, cache_nope,
+    cache_rope, nope, rope), caches as float64 [slots, width] after the write, rows float64.
+    tokens: optional index array restricting the write to those tokens (for sampling)."""
+    from oracle import latent_write as lw
+
+    slots = oracle_slots(orc, case)
+    cn = to_f64(case.cache_nope, case.dtype).reshape(-1, 512)
+    cr = to_f64(case.cache_rope, case.dtype).reshape(-1, 64)
+    sel = slice(None) if tokens is None else tokens
+    nope, rope = lw.latent_write(to_f64(case.latent[sel], case.dtype), to_f64(case.gamma, case.dtype),
+                                 to_f64(case.cos[sel], case.dtype), to_f64(case.sin[sel], case.dtype),
+                                 slots[sel], case.eps, cn, cr, case.layout)
+    return slots, cn, cr, nope, rope

@@ -285,6 +285,80 @@ def prefill_case(seed: int, B: int, H: int, Hkv: int, D: int, dtype: str, *, cac
                 cu_seqlens_q=cu, null_block=null_block)
 
 
+@dataclasses.dataclass
+class LatentCase:
+    """One call of the fused latent write (RMSNorm + RoPE + paged write, MLA).
+
+    latent [T, 512 + 64] is the KV down-projection's row per new token, gamma [512]
+    the norm weight, cos / sin [T, 64] the rotary inputs at each token's position
+    (the operator takes them as given; here they are the cosines and sines of
+    position x 10000^(-2k/64), k the pair index, laid out for `layout`: 0 = the two
+    halves, 1 = interleaved pairs).  New token i of sequence new_batch_idx[i] sits at
+    position new_pos[i] (-1: a padding token with no slot).  The cache arrays are
+    the MLA latent and rotary caches [num_blocks, block_size, 1, width]."""
+    name: str
+    kind: str
+    dtype: str
+    B: int
+    block_size: int
+    num_blocks: int
+    block_table: np.ndarray
+    new_batch_idx: np.ndarray
+    new_pos: np.ndarray
+    latent: np.ndarray
+    gamma: np.ndarray
+    cos: np.ndarray
+    sin: np.ndarray
+    cache_nope: np.ndarray
+    cache_rope: np.ndarray
+    eps: float
+    layout: int
+    outputs: bool = True
+
+    @property
+    def T(self) -> int:
+        return int(self.new_pos.size)
+
+
+def _to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float32)
+    return x if dtype == "f32" else bf16_bits(x)
+
+
+def latent_case(seed: int, B: int, dtype: str, *, new, cached=0, block_size: int = 128, layout: int = 0,
+                eps: float = 1e-6, pad_every: int = 0, outputs: bool = True, spare_blocks: int = 3,
+                name: str = "latent_write") -> LatentCase:
+    """Sequence b holds cached[b] tokens and gets new[b] more; every pad_every-th
+    token (when > 0) is a padding token.  Draw order: table permutation -> latent ->
+    gamma -> cache pool."""
+    dr = Draws(seed)
+    rng = dr.rng
+    cached = np.broadcast_to(np.asarray(cached, dtype=np.int64), (B,)).copy()
+    new = np.broadcast_to(np.asarray(new, dtype=np.int64), (B,)).copy()
+    total = cached + new
+    max_blocks = max(1, -(-int(total.max(initial=1)) // block_size))
+    nb = B * max_blocks + spare_blocks
+    bt = rng.permutation(nb)[:B * max_blocks].astype(np.int32).reshape(B, max_blocks)
+    bidx = np.repeat(np.arange(B, dtype=np.int32), new)
+    pos = np.concatenate([np.arange(c, c + n) for c, n in zip(cached, new)]).astype(np.int32) \
+        if new.sum() else np.zeros(0, dtype=np.int32)
+    if pad_every > 0:
+        pos[::pad_every] = -1
+    T = pos.size
+    latent = dr.normal((T, 512 + 64), dtype)
+    gamma = _to_dtype(1.0 + 0.25 * dr.normal((512,), "f32"), dtype)
+    cache_nope = dr.normal((nb, block_size, 1, 512), dtype)
+    cache_rope = dr.normal((nb, block_size, 1, 64), dtype)
+    inv = 10000.0 ** (-2.0 * np.arange(32) / 64.0)
+    theta = np.outer(np.maximum(pos, 0).astype(np.float64), inv)
+    theta = np.concatenate([theta, theta], axis=1) if layout == 0 else np.repeat(theta, 2, axis=1)
+    return LatentCase(name=name, kind="latent_write", dtype=dtype, B=B, block_size=block_size, num_blocks=nb,
+                      block_table=bt, new_batch_idx=bidx, new_pos=pos, latent=latent, gamma=gamma,
+                      cos=_to_dtype(np.cos(theta), dtype), sin=_to_dtype(np.sin(theta), dtype),
+                      cache_nope=cache_nope, cache_rope=cache_rope, eps=float(eps), layout=layout,
+                      outputs=outputs)
+
+
 # ---------------------------------------------------------------------------
 # The five workloads at full size.
 # ---------------------------------------------------------------------------
@@ -342,6 +416,14 @@ def mla_chunked_prefill(seed: int = 0) -> Case:
                         scale=1.0 / math.sqrt(576.0), name="mla_chunked_prefill")
 
 
+def mla_latent_write(seed: int = 0) -> LatentCase:
+    """Fused latent write of an MLA prefill: B=8 sequences x 4096 new tokens
+    (32768 rows of latent 512 + rope 64) into a permuted pool of 259 blocks of
+    128, rotate-half RoPE, eps 1e-6, normalised and rotated rows also returned,
+    bf16."""
+    return latent_case(seed, 8, "bf16", new=4096, name="mla_latent_write")
+
+
 WORKLOADS = {
     "tiny_f32_decode": tiny_f32_decode,
     "mha_decode_7b": mha_decode_7b,
@@ -351,4 +433,5 @@ WORKLOADS = {
     "mla_decode": mla_decode,
     "mla_mtp_decode": mla_mtp_decode,
     "mla_chunked_prefill": mla_chunked_prefill,
+    "mla_latent_write": mla_latent_write,
 }
