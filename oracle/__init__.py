@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package.  The HIP library
 never calls it and never falls back to it; the two share no code.
 
-Arrays are numpy: float32 for f32 data, uint16 raw bits for bf16 data, int32 for
-indices.  Results are float64.  What each function computes, and the page each
+Arrays are numpy: float32 for f32 data, uint16 raw bits for bf16 data, float64
+for dequantized int8 caches, int32 for indices.  Results are float64.  What each function computes, and the page each
 step follows, is written in the header comment of ``pkv_oracle.c``.
 """
 from __future__ import annotations
@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pkv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 _ERRORS = {-1: "invalid argument", -2: "index out of range", -3: "out of memory"}
 
@@ -88,6 +88,8 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
+    if a.dtype == np.float64:
+        return F64
     raise TypeError(f"unsupported element array dtype {a.dtype}")
 
 

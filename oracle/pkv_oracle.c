@@ -35,7 +35,9 @@
  * Where a row has no visible key the output row is zero (reading of the
  * skill page's note on fully masked rows).
  *
- * Element types: 0 = IEEE float32, 1 = bfloat16 stored as raw uint16 bits.
+ * Element types: 0 = IEEE float32, 1 = bfloat16 stored as raw uint16 bits,
+ * 2 = IEEE float64 (used for caches dequantized from int8 codes, whose values
+ * k * scale a float32 cannot hold exactly).
  * All tensors are dense row-major host arrays.
  */
 #include <math.h>
@@ -48,6 +50,7 @@
 
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_F64 2
 
 #define OR_OK 0
 #define OR_ERR_ARG (-1)
@@ -71,6 +74,7 @@ typedef struct {
 /* One element widened to double.  bf16 -> f32 is exact (the bf16 bits are
    the top half of the f32 bits); f32 -> double is exact. */
 static double elem(const void* base, int32_t dtype, int64_t i) {
+  if (dtype == OR_F64) return ((const double*)base)[i];
   if (dtype == OR_F32) return (double)((const float*)base)[i];
   uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16;
   float f;
@@ -200,7 +204,7 @@ static int check_cache(const or_cache* c, int32_t num_q_heads) {
   if (c->block_size <= 0 || c->num_blocks <= 0 || c->num_kv_heads <= 0) return OR_ERR_ARG;
   if (c->k_dim <= 0 || c->v_dim <= 0 || c->rope_dim < 0) return OR_ERR_ARG;
   if (c->rope_dim > 0 && !c->k_rope_cache) return OR_ERR_ARG;
-  if (c->dtype != OR_F32 && c->dtype != OR_BF16) return OR_ERR_ARG;
+  if (c->dtype != OR_F32 && c->dtype != OR_BF16 && c->dtype != OR_F64) return OR_ERR_ARG;
   if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return OR_ERR_ARG;
   return OR_OK;
 }
