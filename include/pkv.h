@@ -45,7 +45,7 @@ typedef enum {
   PKV_ERR_HIP = 4          /* a HIP launch or runtime call failed                  */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2 } pkv_dtype;
 
 /* One layer's paged cache.  Standard attention: k_cache and v_cache of width
  * head_dim, k_rope_cache NULL, rope_dim 0.  MLA absorbed form ("KVCache
@@ -53,7 +53,19 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
  * head_dim = kv_lora_rank = 512), v_cache must be the SAME pointer (key =
  * value = cache_nope), k_rope_cache holds the rotary part (cache_rope,
  * [num_blocks, block_size, 1, rope_dim] with rope_dim = 64) and
- * num_kv_heads = 1 -- the constraints that page lists for this mode. */
+ * num_kv_heads = 1 -- the constraints that page lists for this mode.
+ *
+ * INT8 cache (dtype PKV_INT8; the cache quantization the "KV Cache notes"
+ * quantized-cache section and the skill page's advanced features name, which
+ * halves the bytes decode reads): k_cache / v_cache hold int8 codes in the same
+ * [num_blocks, block_size, num_kv_heads, head_dim] layout and k_scale / v_scale
+ * hold one float32 scale per (slot, head) in [num_blocks, num_kv_heads,
+ * block_size] order (the scales of consecutive keys of a head are adjacent).  A
+ * row x of one token and head is stored as s = max|x| / 127 and codes
+ * q = round_half_even(x * (127 / max|x|)) (float32 arithmetic; an all-zero row has
+ * s = 0, q = 0) and stands for q * s.  Queries, new rows and outputs stay bf16.
+ * Standard attention only (no rope part), head_dim 128; kv_cache_write quantizes,
+ * paged_attn_decode reads it (head groups up to 16); prefill does not take it. */
 typedef struct {
   void* k_cache;
   void* v_cache;
@@ -63,7 +75,10 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;     /* 64, 128 or 256; 512 for MLA                                */
   int32_t rope_dim;     /* 0, or 64 for MLA                                           */
-  int32_t dtype;        /* pkv_dtype of every cache tensor and of q / k / v / q_rope */
+  int32_t dtype;        /* pkv_dtype of every cache tensor and of q / k / v / q_rope; */
+                        /* PKV_INT8: int8 caches, bf16 q / k / v                    */
+  void* k_scale;        /* PKV_INT8: float32 [num_blocks, num_kv_heads, block_size]; else NULL */
+  void* v_scale;
 } pkv_paged_cache;
 
 /* Attention parameters.  There are no defaults: a zero or negative scale is an
@@ -96,7 +111,9 @@ pkv_status pkv_resolve_slots(const int32_t* block_table, int32_t batch, int32_t 
 
 /* Cache write ("Ascend NPU standalone-deployment KVCache guide", mode 2: the
  * scatter into the cache viewed as [num_blocks*block_size, num_kv_heads, head_dim]).
- * Row t of k (and v, and k_rope) is copied bit for bit to cache row slot_mapping[t].
+ * Row t of k (and v, and k_rope) is copied bit for bit to cache row slot_mapping[t];
+ * into a PKV_INT8 cache each (token, head) row of the bf16 k and v is quantized
+ * instead (codes to the row, scale to the scale arrays).
  *   slot_mapping : [num_tokens]; a negative slot skips the row.  Slots must be distinct.
  *   k, v         : [num_tokens, num_kv_heads, head_dim]; v must be NULL when
  *                  cache->v_cache == cache->k_cache (MLA latent written once)

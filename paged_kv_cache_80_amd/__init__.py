@@ -22,7 +22,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_INT8 = 0, 1, 2
 PKV_ROPE_HALF, PKV_ROPE_INTERLEAVED = 0, 1
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED", 3: "PKV_ERR_WORKSPACE",
           4: "PKV_ERR_HIP"}
@@ -43,7 +43,8 @@ class PagedCacheDesc(ctypes.Structure):
     _fields_ = [("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
                 ("k_rope_cache", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class AttnParams(ctypes.Structure):
@@ -95,6 +96,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return PKV_F32
     if t.dtype == torch.bfloat16:
         return PKV_BF16
+    if t.dtype == torch.int8:
+        return PKV_INT8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -114,6 +117,14 @@ def _i32(t: torch.Tensor) -> torch.Tensor:
     return t
 
 
+def _check_elems(cache: "PagedKVCache", *ts) -> None:
+    """q / k / v / q_rope take the cache dtype; an int8 cache takes bf16 ones."""
+    want = torch.bfloat16 if cache.k_cache.dtype == torch.int8 else cache.k_cache.dtype
+    for t in ts:
+        if t is not None and t.dtype != want:
+            raise TypeError(f"expected {want} rows for a {cache.k_cache.dtype} cache, got {t.dtype}")
+
+
 def _stream(stream) -> Optional[int]:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -125,10 +136,13 @@ class PagedKVCache:
 
     MLA: k_cache is the latent (cache_nope), v_cache is None (the value is the
     latent itself) and k_rope_cache [num_blocks, block_size, 1, 64] holds the
-    rotary part."""
+    rotary part.  INT8: k_cache / v_cache are int8 codes and k_scale / v_scale
+    float32 [num_blocks, H_kv, block_size] scales."""
     k_cache: torch.Tensor
     v_cache: Optional[torch.Tensor] = None
     k_rope_cache: Optional[torch.Tensor] = None
+    k_scale: Optional[torch.Tensor] = None
+    v_scale: Optional[torch.Tensor] = None
 
     def desc(self) -> PagedCacheDesc:
         k = self.k_cache
@@ -137,8 +151,11 @@ class PagedKVCache:
         if v.shape != k.shape or v.dtype != k.dtype:
             raise ValueError("v_cache must match k_cache in shape and dtype")
         rd = 0 if self.k_rope_cache is None else self.k_rope_cache.shape[3]
+        for sc in (self.k_scale, self.v_scale):
+            if sc is not None and (sc.dtype != torch.float32 or tuple(sc.shape) != (nb, hkv, bs)):
+                raise ValueError("scales must be float32 [num_blocks, num_kv_heads, block_size]")
         return PagedCacheDesc(_ptr(k), _ptr(v), _ptr(self.k_rope_cache), nb, bs, hkv, d, rd,
-                              _dtype_code(k))
+                              _dtype_code(k), _ptr(self.k_scale), _ptr(self.v_scale))
 
 
 def pkv_resolve_slots(block_table: torch.Tensor, block_size: int, batch_idx: torch.Tensor,
@@ -159,6 +176,7 @@ def kv_cache_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: Optional[torc
                    cache: PagedKVCache, k_rope: Optional[torch.Tensor] = None, stream=None) -> None:
     """Copy row t of k (v, k_rope) to cache row slot_mapping[t] (negative slots skip)."""
     d = cache.desc()
+    _check_elems(cache, k, v, k_rope)
     _check(load().kv_cache_write(_ptr(_i32(slot_mapping)), slot_mapping.numel(), _ptr(k), _ptr(v),
                                  _ptr(k_rope), ctypes.byref(d), _stream(stream)))
 
@@ -200,6 +218,7 @@ def paged_attn_decode(q: torch.Tensor, cache: PagedKVCache, block_table: torch.T
                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """q [B, H, D] -> out [B, H, D]; seq_lens counts keys including this step's token."""
     B, H, D = q.shape
+    _check_elems(cache, q, q_rope)
     if out is None:
         out = torch.empty((B, H, D), dtype=out_dtype or q.dtype, device=q.device)
     d = cache.desc()
@@ -223,6 +242,7 @@ def paged_attn_prefill(q: torch.Tensor, cache: PagedKVCache, block_table: torch.
     """q TND [T, H, D] -> out [T, H, D], bottom-right causal over each sequence's keys."""
     T, H, D = q.shape
     B = cu_seqlens_q.numel() - 1
+    _check_elems(cache, q, q_rope)
     if out is None:
         out = torch.empty((T, H, D), dtype=out_dtype or q.dtype, device=q.device)
     d = cache.desc()

@@ -38,9 +38,11 @@ pkv_status from_hip(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+int elem_bytes(int32_t dtype) { return dtype == PKV_INT8 ? 1 : dtype == PKV_BF16 ? 2 : 4; }
 
 bool valid_dtype(int32_t d) { return d == PKV_F32 || d == PKV_BF16; }
+
+bool is_int8(const pkv_paged_cache* c) { return c->dtype == PKV_INT8; }
 
 bool pow2_block(int32_t bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
 
@@ -52,7 +54,8 @@ bool is_mla(const pkv_paged_cache* c) { return c->rope_dim > 0; }
 pkv_status check_cache(const pkv_paged_cache* c) {
   if (!c) return fail(PKV_ERR_INVALID_ARG, "cache is NULL");
   if (!c->k_cache || !c->v_cache) return fail(PKV_ERR_INVALID_ARG, "k_cache / v_cache is NULL");
-  if (!valid_dtype(c->dtype)) return fail(PKV_ERR_INVALID_ARG, "cache dtype %d is not f32 or bf16", c->dtype);
+  if (!valid_dtype(c->dtype) && c->dtype != PKV_INT8)
+    return fail(PKV_ERR_INVALID_ARG, "cache dtype %d is not f32, bf16 or int8", c->dtype);
   if (c->num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks %d must be > 0", c->num_blocks);
   if (!pow2_block(c->block_size))
     return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not one of 16, 32, 64, 128", c->block_size);
@@ -67,6 +70,16 @@ pkv_status check_cache(const pkv_paged_cache* c) {
     return fail(PKV_ERR_UNSUPPORTED, "a rope row is not a multiple of 16 bytes");
   if (!aligned16(c->k_cache) || !aligned16(c->v_cache) || (c->k_rope_cache && !aligned16(c->k_rope_cache)))
     return fail(PKV_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+  if (is_int8(c)) {
+    if (!c->k_scale || !c->v_scale) return fail(PKV_ERR_INVALID_ARG, "int8 cache: k_scale / v_scale is NULL");
+    if (!aligned16(c->k_scale) || !aligned16(c->v_scale))
+      return fail(PKV_ERR_INVALID_ARG, "int8 cache: scale pointers must be 16-byte aligned");
+    if (is_mla(c)) return fail(PKV_ERR_UNSUPPORTED, "int8 cache: no rope part (standard attention only)");
+    if (c->v_cache == c->k_cache) return fail(PKV_ERR_INVALID_ARG, "int8 cache: k_cache and v_cache must differ");
+    if (c->head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "int8 cache: head_dim must be 128 (got %d)", c->head_dim);
+  } else if (c->k_scale || c->v_scale) {
+    return fail(PKV_ERR_INVALID_ARG, "k_scale / v_scale apply to int8 caches only");
+  }
   if (is_mla(c)) {
     // "KVCache optimisation skill", mode 3 constraints: key = value = cache_nope,
     // rope D = 64, latent width 512, a single latent head.
@@ -229,6 +242,20 @@ pkv_status kv_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const
     return fail(PKV_ERR_INVALID_ARG, "k_rope must be given exactly when the cache has a rope part");
   if (!aligned16(k) || (v && !aligned16(v)) || (k_rope && !aligned16(k_rope)))
     return fail(PKV_ERR_INVALID_ARG, "k / v / k_rope must be 16-byte aligned");
+  if (is_int8(cache)) {
+    pkv::Int8WriteArgs w{};
+    w.k = k;
+    w.v = v;
+    w.k_cache = cache->k_cache;
+    w.v_cache = cache->v_cache;
+    w.k_scale = static_cast<float*>(cache->k_scale);
+    w.v_scale = static_cast<float*>(cache->v_scale);
+    w.num_tokens = num_tokens;
+    w.num_kv_heads = cache->num_kv_heads;
+    w.block_size_log2 = log2i(cache->block_size);
+    return from_hip(pkv::launch_cache_write_int8(slot_mapping, w, static_cast<hipStream_t>(stream)),
+                    "kv_cache_write launch");
+  }
   pkv::WriteRows rows{};
   const int32_t eb = elem_bytes(cache->dtype);
   rows.src[0] = k;
@@ -351,6 +378,8 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
     }
     return ok();
   }
+  if (!plan.stream && is_int8(cache))
+    return fail(PKV_ERR_UNSUPPORTED, "int8 decode: needs head groups of at most 16 (got %d)", group);
   if (!plan.stream && !pkv::decode_valu_supported(cache->dtype, cache->head_dim, group))
     return fail(PKV_ERR_UNSUPPORTED, "decode: dtype %d, head_dim %d, group %d not supported", cache->dtype,
                 cache->head_dim, group);
@@ -375,6 +404,8 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
   a.scale_log2e = params->scale * pkv::kLog2e;
   a.dtype = cache->dtype;
   a.out_dtype = params->out_dtype;
+  a.k_scale = static_cast<const float*>(cache->k_scale);
+  a.v_scale = static_cast<const float*>(cache->v_scale);
   if (plan.stream) {
     // bf16 with 128-wide heads: matrix-core decode over a stream split (any head
     // group: the group is a dense contraction and every K/V row is read once).
@@ -413,6 +444,7 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
   if (s) return s;
   if (total_q < 0 || max_q_len < 0) return fail(PKV_ERR_INVALID_ARG, "total_q and max_q_len must be >= 0");
   if (params->split_tokens != 0) return fail(PKV_ERR_INVALID_ARG, "split_tokens applies to decode only");
+  if (is_int8(cache)) return fail(PKV_ERR_UNSUPPORTED, "prefill does not read int8 caches");
   if (params->batch == 0 || total_q == 0) return ok();
   if (!q || !block_table || !cu_seqlens_q || !seq_lens_kv || !out)
     return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");

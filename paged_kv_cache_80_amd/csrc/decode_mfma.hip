@@ -49,6 +49,16 @@
 // exact (O and l share it) and skips the O rescale on almost every tile.
 // Probabilities enter P.V as a hi + lo bf16 pair (p = hi + lo + r, |r| < 2^-15
 // p), so rounding P costs no accuracy.
+//
+// INT8 caches (I8).  A tile then holds 32 rows of 128 int8 codes per tensor
+// (4 KiB) plus the 32 K and 32 V scales of the tile's keys (256 bytes, one more
+// DMA).  Codes become bf16 in registers after the LDS read (exact: at most 8
+// significant bits), so the same MFMAs run: S^T = Kq.Q^T is scaled per key by
+// its K scale, and the V scales fold into P before the hi/lo split
+// (sum_j p_j s_j v_j = (p . s) . Vq).  V^T operands come from the byte
+// transposing read ds_read_b64_tr_b8, which hands a lane 8 consecutive keys of
+// one dim; to match, the K operand rows are ordered so that S^T lane (n, lg)
+// holds keys 8 lg .. 8 lg + 7 (tile u row m is key 8 (m / 4) + 4 u + m % 4).
 #include "mfma_common.h"
 #include "pkv_internal.h"
 
@@ -59,15 +69,29 @@ constexpr int kD = 128;
 constexpr int kKeyTile = 32;
 constexpr int kTileLog2 = 5;
 constexpr int kRowBytes = kD * 2;                 // 256: one head row of K or V
-constexpr int kTileBytes = kKeyTile * kRowBytes;  // 8 KiB: one tensor of one tile
 constexpr int kWaves = 4;                         // independent waves per workgroup
-constexpr int kSlotBytes = 2 * kTileBytes;        // K then V of one tile
 constexpr float kRescaleLog2 = 8.f;
+
+// Tile geometry per cache type: bytes of one head row, of one tensor of a tile,
+// of a whole LDS slot (K, V and, for int8, the tile's 32 + 32 scales), and the
+// DMA instructions that fill a slot.
+template <bool I8>
+struct Geo {
+  static constexpr int kRow = I8 ? kD : 2 * kD;
+  static constexpr int kTile = kKeyTile * kRow;
+  static constexpr int kSlot = 2 * kTile + (I8 ? 2 * kKeyTile * 4 : 0);
+  static constexpr int kDma = I8 ? 9 : 16;
+};
 constexpr int kLdsPrefix = 2048;                   // batch + 1 up to this: prefix scanned in LDS
 
 // 16-byte chunk swizzles of row r in the staged K and V tiles.
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
+// int8 tiles (8 chunks per 128-byte row): K rows of one operand read (rows
+// 8 m + 4 u + e, m, e < 4) land in 8 distinct chunk positions per bank half; V
+// rows of one transposing read (8 consecutive rows) in 8 distinct positions.
+__device__ __forceinline__ int kswz8(int r) { return 2 * ((r >> 3) & 3) + ((r >> 1) & 1); }
+__device__ __forceinline__ int vswz8(int r) { return r & 7; }
 
 // Scalar (SMEM) load of a value that is uniform across the wave and read-only
 // for the whole kernel.  Vector loads retire in order, so a vector load of
@@ -136,11 +160,12 @@ struct Cursor {
 // LDS_PREFIX: every workgroup scans seq_lens into its own LDS copy of the
 // column prefix (batch + 1 <= kLdsPrefix) and workgroup 0 also stores it for
 // the combine; otherwise tile_prefix_kernel has written it to the workspace.
-template <bool ONE_BLOCK, bool LDS_PREFIX>
+template <bool ONE_BLOCK, bool LDS_PREFIX, bool I8>
 __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(DecodeArgs a) {
   constexpr int KS = kD / 32;  // contraction steps of q.k
   constexpr int DT = kD / 16;  // 16-row tiles of O^T
-  __shared__ __attribute__((aligned(16))) unsigned char lds_buf[kWaves * 2 * kSlotBytes];
+  using GT = Geo<I8>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_buf[kWaves * 2 * GT::kSlot];
   __shared__ int32_t s_prefix[LDS_PREFIX ? kLdsPrefix : 1];
   __shared__ int32_t s_wave_sum[kWaves];
 
@@ -233,11 +258,13 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
   };
 
   const int64_t row_elems = (int64_t)Hkv * kD;  // elements between consecutive slots
-  const uint32_t row_bytes = (uint32_t)row_elems * 2;
+  const uint32_t row_bytes = (uint32_t)row_elems * (I8 ? 1 : 2);
   const int bs_log2 = a.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const uint16_t* kcache = static_cast<const uint16_t*>(a.k_cache);
   const uint16_t* vcache = static_cast<const uint16_t*>(a.v_cache);
+  const unsigned char* kcache8 = static_cast<const unsigned char*>(a.k_cache);
+  const unsigned char* vcache8 = static_cast<const unsigned char*>(a.v_cache);
 
   // Lane constants.  DMA instruction i of a tensor fills rows 4i + lg; lane
   // (l16, lg) fills chunk position l16 and so reads logical chunk l16 ^ swz(r),
@@ -257,7 +284,29 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
   int vr_off[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) vr_off[dt] = ra * kRowBytes + 32 * (dt ^ (ra & 7)) + 8 * (l16 & 3);
-  unsigned char* slots = lds_buf + wave * 2 * kSlotBytes;
+  // int8: DMA instruction i of K fills rows 8i + lane/8, chunk position lane % 8
+  // (logical chunk (lane % 8) ^ kswz8(row)); V likewise with vswz8(row) = lane / 8.
+  // K operand (tile u, step ks): row 8(l16/4) + 4u + l16%4, bytes 32ks + 8lg.
+  // V^T operand of dim tile dt: the transposing read of row 8lg + l16/2, half
+  // l16 % 2 of logical chunk dt.
+  uint32_t k_src8[4], v_src8 = 0;
+  int kr8_off[2][KS], vr8_off[DT];
+  if constexpr (I8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) k_src8[i] = 16 * ((lane & 7) ^ kswz8(8 * i + (lane >> 3)));
+    v_src8 = 16 * ((lane & 7) ^ vswz8(lane >> 3));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r = 8 * (l16 >> 2) + 4 * u + (l16 & 3);
+        kr8_off[u][ks] = r * GT::kRow + 16 * ((2 * ks + (lg >> 1)) ^ kswz8(r)) + 8 * (lg & 1);
+      }
+    const int rv = 8 * lg + (l16 >> 1);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vr8_off[dt] = rv * GT::kRow + 16 * (dt ^ vswz8(rv)) + 8 * (l16 & 1);
+  }
+  unsigned char* slots = lds_buf + wave * 2 * GT::kSlot;
 
   // Copy the tile at cursor c (16 DMAs: K rows then V rows) into slot `sl`.
   // Rows outside [lo, L) re-read a visible row of the tile: they are masked
@@ -269,9 +318,52 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
     const int hi_r = min(c.L - t0, kKeyTile) - 1;
     const int32_t* bt = a.block_table + (int64_t)c.b * a.max_blocks_per_seq;
     const int64_t head_off = (int64_t)g * kD;
-    unsigned char* kdst = slots + sl * kSlotBytes;
-    unsigned char* vdst = kdst + kTileBytes;
-    if constexpr (ONE_BLOCK) {  // one table entry, a wave-uniform base and 32-bit lane offsets
+    unsigned char* kdst = slots + sl * GT::kSlot;
+    unsigned char* vdst = kdst + GT::kTile;
+    if constexpr (I8) {
+      // 4 + 4 row DMAs (8 rows of 128 codes each) and one for the scales: lanes
+      // 0..7 bring the K scales of keys 4l .. 4l + 3, lanes 8..15 the V scales.
+      // Scales of keys outside [lo, L) are read too (in bounds: the tile's
+      // block(s)) and masked out in compute; rows are clamped as below.
+      unsigned char* sdst = vdst + GT::kTile;
+      const int blk = t0 >> bs_log2;
+      const float* scale_src = lane < 8 ? a.k_scale : a.v_scale;
+      const int key = 4 * (lane & 7);
+      if constexpr (ONE_BLOCK) {
+        const int32_t phys = sload(bt + blk);
+        const int64_t row0 = ((int64_t)phys << bs_log2) + (t0 & bs_mask);
+        const unsigned char* kb = kcache8 + row0 * row_bytes + head_off;
+        const unsigned char* vb = vcache8 + row0 * row_bytes + head_off;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t row = (uint32_t)min(max(8 * i + (lane >> 3), lo_r), hi_r) * row_bytes;
+          load_lds16_s(kb, row + k_src8[i], kdst + 1024 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t row = (uint32_t)min(max(8 * i + (lane >> 3), lo_r), hi_r) * row_bytes;
+          load_lds16_s(vb, row + v_src8, vdst + 1024 * i);
+        }
+        if (lane < 16)
+          load_lds16(scale_src + ((((int64_t)phys * Hkv + g) << bs_log2) + (t0 & bs_mask) + key), sdst);
+      } else {
+        const int32_t e0 = sload(bt + blk);
+        const int32_t e1 = ((blk + 1) << bs_log2) < c.L ? sload(bt + blk + 1) : e0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = t0 + min(max(8 * i + (lane >> 3), lo_r), hi_r);
+          const int32_t phys = (j >> bs_log2) == blk ? e0 : e1;
+          const int64_t slot = ((int64_t)phys << bs_log2) + (j & bs_mask);
+          load_lds16(kcache8 + slot * row_bytes + head_off + k_src8[i], kdst + 1024 * i);
+          load_lds16(vcache8 + slot * row_bytes + head_off + v_src8, vdst + 1024 * i);
+        }
+        if (lane < 16) {
+          const int j = t0 + key;  // the lane's 4 keys lie in one 16-key block
+          const int32_t phys = (j >> bs_log2) == blk ? e0 : e1;
+          load_lds16(scale_src + ((((int64_t)phys * Hkv + g) << bs_log2) + (j & bs_mask)), sdst);
+        }
+      }
+    } else if constexpr (ONE_BLOCK) {  // one table entry, a wave-uniform base and 32-bit lane offsets
       const int32_t phys = sload(bt + (t0 >> bs_log2));
       const int64_t row0 = ((int64_t)phys << bs_log2) + (t0 & bs_mask);
       const uint16_t* kb = kcache + row0 * row_elems + head_off;
@@ -342,10 +434,88 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
 
   const float c2 = a.scale_log2e;
   // Compute the tile at cursor c from slot `sl`.
+  auto compute_i8 = [&](const Cursor& c, int sl) {
+    const int t0 = c.t_first + (c.k << kTileLog2);
+    const unsigned char* kt = slots + sl * GT::kSlot;
+    const unsigned char* vt = kt + GT::kTile;
+    const float* sc = reinterpret_cast<const float*>(vt + GT::kTile);  // 32 K scales, then 32 V scales
+
+    f32x4_t s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 af = i8x8_to_bf16(*reinterpret_cast<const uint2*>(kt + kr8_off[u][ks]));
+        s[u] = mfma_bf16(af, qf[ks], ks == 0 ? f32x4_zero() : s[u]);
+      }
+    }
+    // Lane (n, lg) holds keys 8 lg + 4 u + e of tile u.
+    float4 ksc[2], vsc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      ksc[u] = *reinterpret_cast<const float4*>(sc + 8 * lg + 4 * u);
+      vsc[u] = *reinterpret_cast<const float4*>(sc + kKeyTile + 8 * lg + 4 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u][0] *= ksc[u].x;
+      s[u][1] *= ksc[u].y;
+      s[u][2] *= ksc[u].z;
+      s[u][3] *= ksc[u].w;
+    }
+    if (!(t0 >= c.lo && t0 + kKeyTile <= c.L)) {
+      // Keys outside [lo, L): logit -inf and V scale 0 (their scales may be any
+      // bits, a NaN included: selected away, never multiplied).
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float* vs = reinterpret_cast<float*>(&vsc[u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = t0 + 8 * lg + 4 * u + e;
+          const bool ok = j >= c.lo && j < c.L;
+          s[u][e] = ok ? s[u][e] : kNegInf;
+          vs[e] = ok ? vs[e] : 0.f;
+        }
+      }
+    }
+    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mt = row4_max(mt);
+    const float mts = mt * c2;
+    const bool raise = mts > mref + kRescaleLog2;
+    if (__any(raise)) {
+      const float alpha = raise ? exp2_fast(mref - mts) : 1.f;
+      if (raise) mref = mts;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    const float mb = mref == kNegInf ? 0.f : mref;
+    float pv[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float* vs = reinterpret_cast<const float*>(&vsc[u]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = exp2_fast(fmaf(s[u][e], c2, -mb));
+        l += p;
+        pv[4 * u + e] = p * vs[e];
+      }
+    }
+    uint4 phi, plo;
+    pack_p_split(pv, phi, plo);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint4 af = i8x8_to_bf16(lds_tr8(vt + vr8_off[dt]));
+      o[dt] = mfma_bf16(af, phi, o[dt]);
+      o[dt] = mfma_bf16(af, plo, o[dt]);
+    }
+  };
+
   auto compute = [&](const Cursor& c, int sl) {
     const int t0 = c.t_first + (c.k << kTileLog2);
-    const unsigned char* kt = slots + sl * kSlotBytes;
-    const unsigned char* vt = kt + kTileBytes;
+    const unsigned char* kt = slots + sl * GT::kSlot;
+    const unsigned char* vt = kt + GT::kTile;
 
     f32x4_t s[2];
 #pragma unroll
@@ -414,11 +584,12 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
     if (i + 1 < ntl) {
       advance(pc);
       issue_tile(pc, sl ^ 1);
-      wait_vm<16>();  // tile i has landed; tile i + 1's 16 copies stay in flight
+      wait_vm<GT::kDma>();  // tile i has landed; tile i + 1's copies stay in flight
     } else {
       wait_vm<0>();
     }
-    compute(cc, sl);
+    if constexpr (I8) compute_i8(cc, sl);
+    else compute(cc, sl);
     if (i + 1 < ntl) {
       const Cursor prev = cc;
       advance(cc);
@@ -508,7 +679,7 @@ __global__ __launch_bounds__(kWaves * kWave) void stream_combine_kernel(DecodeAr
 }  // namespace
 
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
-  return dtype == PKV_BF16 && head_dim == kD && group >= 1 && group <= 16;
+  return (dtype == PKV_BF16 || dtype == PKV_INT8) && head_dim == kD && group >= 1 && group <= 16;
 }
 
 int32_t decode_stream_resident_waves(int32_t cu_count) { return cu_count * kWaves; }
@@ -534,14 +705,18 @@ hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream) {
   }
   const unsigned grid = (unsigned)(a.resident_waves / kWaves);
   const bool one_block = a.block_size_log2 >= kTileLog2;
-  if (lds_prefix && one_block)
-    decode_stream_kernel<true, true><<<grid, kWaves * kWave, 0, stream>>>(a);
-  else if (lds_prefix)
-    decode_stream_kernel<false, true><<<grid, kWaves * kWave, 0, stream>>>(a);
-  else if (one_block)
-    decode_stream_kernel<true, false><<<grid, kWaves * kWave, 0, stream>>>(a);
-  else
-    decode_stream_kernel<false, false><<<grid, kWaves * kWave, 0, stream>>>(a);
+  const dim3 blk(kWaves * kWave);
+  if (a.dtype == PKV_INT8) {
+    if (lds_prefix && one_block) decode_stream_kernel<true, true, true><<<grid, blk, 0, stream>>>(a);
+    else if (lds_prefix) decode_stream_kernel<false, true, true><<<grid, blk, 0, stream>>>(a);
+    else if (one_block) decode_stream_kernel<true, false, true><<<grid, blk, 0, stream>>>(a);
+    else decode_stream_kernel<false, false, true><<<grid, blk, 0, stream>>>(a);
+  } else {
+    if (lds_prefix && one_block) decode_stream_kernel<true, true, false><<<grid, blk, 0, stream>>>(a);
+    else if (lds_prefix) decode_stream_kernel<false, true, false><<<grid, blk, 0, stream>>>(a);
+    else if (one_block) decode_stream_kernel<true, false, false><<<grid, blk, 0, stream>>>(a);
+    else decode_stream_kernel<false, false, false><<<grid, blk, 0, stream>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)a.batch * a.num_q_heads;

@@ -184,6 +184,34 @@ __device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Transposing LDS read of bytes (ds_read_b64_tr_b8): within each group of 16
+// lanes, lane i receives byte (i % 8) of the 8-byte reads of lanes 2k + i/8,
+// k = 0..7.  If lane j of a group reads row R0 + j/2 at column C0 + 8*(j%2) of a
+// row-major byte tile, lane i gets tile[R0 + k][C0 + i], k = 0..7.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+__device__ __forceinline__ uint2 lds_tr8(const void* p) {
+  const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Eight int8 values (bytes 0..7 of w) as eight bf16 (exact: |q| <= 128 needs at
+// most 8 significant bits).  Each byte is sign-extended and converted to f32,
+// whose top half is the bf16.
+__device__ __forceinline__ uint4 i8x8_to_bf16(const uint2& w) {
+  uint32_t o[4];
+  const uint32_t u[2] = {w.x, w.y};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int32_t x = (int32_t)u[k];
+    const float f0 = (float)((x << 24) >> 24), f1 = (float)((x << 16) >> 24);
+    const float f2 = (float)((x << 8) >> 24), f3 = (float)(x >> 24);
+    o[2 * k] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    o[2 * k + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __device__ __forceinline__ uint4 lds16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 lds8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 

@@ -24,6 +24,19 @@ struct WriteRows {
 hipError_t launch_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const WriteRows& rows,
                               hipStream_t stream);
 
+// Quantizing cache write into an int8 cache (write.hip): every (token, head) row
+// of 128 bf16 values of k and v becomes 128 int8 codes and one float32 scale.
+struct Int8WriteArgs {
+  const void* k;      // [num_tokens, num_kv_heads, 128] bf16
+  const void* v;
+  void* k_cache;      // [slots, num_kv_heads, 128] int8
+  void* v_cache;
+  float* k_scale;     // [num_blocks, num_kv_heads, block_size]
+  float* v_scale;
+  int32_t num_tokens, num_kv_heads, block_size_log2;
+};
+hipError_t launch_cache_write_int8(const int32_t* slot_mapping, const Int8WriteArgs& a, hipStream_t stream);
+
 // Fused RMSNorm + RoPE + cache write of the MLA latent (latent_write.hip).
 // Latent width 512, rotary width 64, one latent head; every array in one dtype.
 struct LatentWriteArgs {
@@ -65,11 +78,15 @@ struct DecodeArgs {
   int32_t* tile_prefix;
   int32_t resident_waves;
   int32_t split_tiles;
+  // int8 caches (dtype PKV_INT8, stream split only): per (slot, head) scales in
+  // [num_blocks, num_kv_heads, block_size] order.
+  const float* k_scale;
+  const float* v_scale;
 };
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);
 // The same decode on the matrix cores with a stream split (decode_mfma.hip):
-// bf16, head_dim 128, head groups up to 16.  Launches the tile scan, the decode
+// bf16 or int8 caches, head_dim 128, head groups up to 16.  Launches the tile scan, the decode
 // and the piece combine.
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
 int32_t decode_stream_resident_waves(int32_t cu_count);

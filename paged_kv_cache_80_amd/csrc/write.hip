@@ -44,6 +44,55 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const int32_t* __restr
   }
 }
 
+// Quantizing write into an int8 cache.  One group of 16 lanes per (token, head)
+// row of 128 values; every lane holds 8 of them.  The row's scale is
+// s = max|x| / 127 and its codes are rint(x * (127 / max|x|)) (both quotients
+// IEEE float32, ties of rint to even), which leaves every code in [-127, 127];
+// an all-zero row gets s = 0 and zero codes.  Groups take the K rows of all
+// tokens first, then the V rows.
+__global__ __launch_bounds__(256) void cache_write_int8_kernel(const int32_t* __restrict__ slot_mapping,
+                                                               Int8WriteArgs a) {
+  constexpr int kD = 128;
+  const int64_t grp = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  const int64_t rows = (int64_t)a.num_tokens * a.num_kv_heads;  // rows of one tensor
+  if (grp >= 2 * rows) return;                                  // whole groups leave together
+  const bool is_v = grp >= rows;
+  const int64_t r = is_v ? grp - rows : grp;
+  const int64_t t = r / a.num_kv_heads;
+  const int h = (int)(r - t * a.num_kv_heads);
+  const int32_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  const uint4 w = ld16(static_cast<const uint16_t*>(is_v ? a.v : a.k) + r * kD + 8 * l);
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = bf16_lo(u[k]);
+    x[2 * k + 1] = bf16_hi(u[k]);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  m = group_max<16>(m);
+  const float scale = m / 127.f;
+  const float inv = m > 0.f ? 127.f / m : 0.f;
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = (int)fminf(fmaxf(rintf(x[e] * inv), -127.f), 127.f);
+    packed[e >> 2] |= ((uint32_t)c & 0xffu) << (8 * (e & 3));
+  }
+  char* dst = static_cast<char*>(is_v ? a.v_cache : a.k_cache) + ((int64_t)slot * a.num_kv_heads + h) * kD + 8 * l;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
+  if (l == 0) {
+    const int32_t blk = slot >> a.block_size_log2;
+    const int32_t off = slot & ((1 << a.block_size_log2) - 1);
+    float* sc = is_v ? a.v_scale : a.k_scale;
+    sc[(((int64_t)blk * a.num_kv_heads + h) << a.block_size_log2) + off] = scale;
+  }
+}
+
 hipError_t launch_resolve_slots(const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
                                 int32_t block_size, const int32_t* batch_idx, const int32_t* pos,
                                 int32_t n, int32_t* slots_out, hipStream_t stream) {
@@ -59,6 +108,13 @@ hipError_t launch_cache_write(const int32_t* slot_mapping, int32_t num_tokens, c
                               hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   cache_write_kernel<<<num_tokens, 256, 0, stream>>>(slot_mapping, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write_int8(const int32_t* slot_mapping, const Int8WriteArgs& a, hipStream_t stream) {
+  const int64_t groups = 2 * (int64_t)a.num_tokens * a.num_kv_heads;
+  if (groups == 0) return hipSuccess;
+  cache_write_int8_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, stream>>>(slot_mapping, a);
   return hipGetLastError();
 }
 

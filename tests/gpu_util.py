@@ -29,12 +29,35 @@ def as_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def int8_device_cache(case) -> "pkv.PagedKVCache":
+    """An int8 cache holding the case's bf16 pools, quantized on the GPU by kv_cache_write
+    (every slot; with a null block, block 0 keeps zero codes and gets NaN scales)."""
+    nb, bs, hkv, d = case.k_cache.shape
+    cache = pkv.PagedKVCache(torch.zeros((nb, bs, hkv, d), dtype=torch.int8, device="cuda"),
+                             torch.zeros((nb, bs, hkv, d), dtype=torch.int8, device="cuda"), None,
+                             torch.zeros((nb, hkv, bs), dtype=torch.float32, device="cuda"),
+                             torch.zeros((nb, hkv, bs), dtype=torch.float32, device="cuda"))
+    slots = torch.arange(nb * bs, dtype=torch.int32, device="cuda")
+    if case.null_block:
+        slots[:bs] = -1
+    pk, pv = dev(case.k_cache), dev(case.v_cache)
+    pkv.kv_cache_write(slots, pk.view(nb * bs, hkv, d), pv.view(nb * bs, hkv, d), cache)
+    if case.null_block:
+        cache.k_scale[0] = float("nan")
+        cache.v_scale[0] = float("nan")
+    torch.cuda.synchronize()
+    return cache
+
+
 class DeviceCase:
     """The device copy of a case's tensors."""
 
     def __init__(self, case):
         self.case = case
-        self.cache = pkv.PagedKVCache(dev(case.k_cache), dev(case.v_cache), dev(case.k_rope_cache))
+        if case.int8:
+            self.cache = int8_device_cache(case)
+        else:
+            self.cache = pkv.PagedKVCache(dev(case.k_cache), dev(case.v_cache), dev(case.k_rope_cache))
         self.block_table = dev(case.block_table)
         self.seq_lens = dev(case.seq_lens)
         self.q = dev(case.q)

@@ -42,8 +42,53 @@ def oracle_attend(orc, case, units=None, want_probs=False, nthreads=0):
                              want_probs=want_probs, nthreads=nthreads)
 
 
+def int8_state(case):
+    """The case's bf16 pools as int8 caches: (k_codes, k_scales, v_codes, v_scales).  With a
+    null block, block 0 holds zero codes and NaN scales (it is never quantized)."""
+    from oracle import int8_cache as q8
+
+    out = []
+    for pool in (case.k_cache, case.v_cache):
+        src = pool
+        if case.null_block:
+            src = pool.copy()
+            src[0] = 0
+        c, sc = q8.quantize_cache(src, case.dtype)
+        if case.null_block:
+            c[0] = 0
+            sc[0] = np.float32("nan")
+        out += [c, sc]
+    return tuple(out)
+
+
+def oracle_write_int8(orc, case, state, slots) -> None:
+    """Quantize the case's new rows into the int8 state (in place)."""
+    from oracle import int8_cache as q8
+
+    kc, ks, vc, vs = state
+    q8.write_rows(kc, ks, slots, case.new_k, case.dtype)
+    q8.write_rows(vc, vs, slots, case.new_v, case.dtype)
+
+
+def oracle_attend_int8(orc, case, state, units=None, nthreads=0):
+    """Decode attention over the dequantized int8 cache (float64)."""
+    from oracle import int8_cache as q8
+
+    kc, ks, vc, vs = state
+    kd, vd = q8.dequantize_cache(kc, ks), q8.dequantize_cache(vc, vs)
+    return orc.paged_decode(to_f64(case.q, case.dtype), kd, vd, case.block_table, case.seq_lens, case.scale,
+                            case.window, units=units, nthreads=nthreads)
+
+
 def oracle_run(orc, case, units=None, want_probs=False, inplace=False, nthreads=0):
-    """resolve -> write -> attend on the CPU.  Returns (out, written_case, slots)."""
+    """resolve -> write -> attend on the CPU.  Returns (out, written_case, slots); for an int8
+    case the second item is the int8 state (k_codes, k_scales, v_codes, v_scales) after the write."""
+    if case.int8:
+        assert case.kind == "decode" and not want_probs
+        slots = oracle_slots(orc, case)
+        state = int8_state(case)
+        oracle_write_int8(orc, case, state, slots)
+        return oracle_attend_int8(orc, case, state, units=units, nthreads=nthreads), state, slots
     c = case if inplace else case.copy_caches()
     slots = oracle_slots(orc, c)
     oracle_write(orc, c, slots)

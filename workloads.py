@@ -141,6 +141,7 @@ class Case:
     window: int = 0
     cu_seqlens_q: Optional[np.ndarray] = None
     null_block: bool = False
+    int8: bool = False  # the cache is stored as int8 codes + scales, quantized from these bf16 values
 
     @property
     def max_blocks(self) -> int:
@@ -205,7 +206,7 @@ def decode_case(seed: int, B: int, H: int, Hkv: int, D: int, dtype: str, *, bloc
                 max_blocks: int, seq_lens=None, len_range=None, window: int = 0,
                 null_block: bool = False, spare_frac: float = 0.1, rope_dim: int = 0,
                 scale: Optional[float] = None, table: Optional[np.ndarray] = None,
-                name: str = "decode") -> Case:
+                int8: bool = False, name: str = "decode") -> Case:
     """Decode case: one new token per sequence at position seq_lens[b] - 1."""
     dr = Draws(seed)
     rng = dr.rng
@@ -240,7 +241,7 @@ def decode_case(seed: int, B: int, H: int, Hkv: int, D: int, dtype: str, *, bloc
                 new_k=new_k, new_v=new_v, new_k_rope=new_k_rope,
                 new_batch_idx=np.arange(B, dtype=np.int32),
                 new_pos=(seq_lens - 1).astype(np.int32), scale=float(scale),
-                window=window, null_block=null_block)
+                window=window, null_block=null_block, int8=int8)
 
 
 def prefill_case(seed: int, B: int, H: int, Hkv: int, D: int, dtype: str, *, cached, new,
@@ -370,20 +371,23 @@ def tiny_f32_decode(seed: int = 0) -> Case:
                        table=np.arange(8, dtype=np.int32).reshape(2, 4), name="tiny_f32_decode")
 
 
-def mha_decode_7b(seed: int = 0) -> Case:
+def mha_decode_7b(seed: int = 0, int8: bool = False) -> Case:
     """llama2-7B single layer: B=64, H=H_kv=32, d_h=128, every length 2048,
-    table = a permutation of 1024 blocks, bf16."""
+    table = a permutation of 1024 blocks, bf16 (int8: the same values held in an
+    int8 cache)."""
     return decode_case(seed, 64, 32, 32, 128, "bf16", max_blocks=16,
-                       seq_lens=np.full(64, 2048, dtype=np.int32), name="mha_decode_7b")
+                       seq_lens=np.full(64, 2048, dtype=np.int32), int8=int8,
+                       name="mha_decode_7b" + ("_int8" if int8 else ""))
 
 
-def gqa_decode_70b(seed: int = 0, window: int = 0) -> Case:
+def gqa_decode_70b(seed: int = 0, window: int = 0, int8: bool = False) -> Case:
     """llama2-70B single layer: B=32, H=64, H_kv=8, d_h=128, lengths uniform in
     [1024, 32768], shuffled table over a pool with 10% spare blocks and null
-    block 0; with window=4096 the blocks wholly before the window are null."""
+    block 0; with window=4096 the blocks wholly before the window are null.
+    int8: the same values held in an int8 cache (codes + per-(token, head) scales)."""
     return decode_case(seed, 32, 64, 8, 128, "bf16", max_blocks=256, len_range=(1024, 32768),
-                       window=window, null_block=True, spare_frac=0.1,
-                       name="gqa_decode_70b" + ("_window%d" % window if window else ""))
+                       window=window, null_block=True, spare_frac=0.1, int8=int8,
+                       name="gqa_decode_70b" + ("_window%d" % window if window else "") + ("_int8" if int8 else ""))
 
 
 def chunked_prefill(seed: int = 0) -> Case:
@@ -429,6 +433,8 @@ WORKLOADS = {
     "mha_decode_7b": mha_decode_7b,
     "gqa_decode_70b": gqa_decode_70b,
     "gqa_decode_70b_window4096": lambda seed=0: gqa_decode_70b(seed, window=4096),
+    "mha_decode_7b_int8": lambda seed=0: mha_decode_7b(seed, int8=True),
+    "gqa_decode_70b_int8": lambda seed=0: gqa_decode_70b(seed, int8=True),
     "chunked_prefill": chunked_prefill,
     "mla_decode": mla_decode,
     "mla_mtp_decode": mla_mtp_decode,
