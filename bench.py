@@ -82,7 +82,11 @@ def algorithmic_bytes(case):
     T = case.new_pos.size
     resolve = T * 16  # batch index, position, table entry, slot
     row = case.Hkv * case.D * eb
-    write = T * (4 + 2 * row * (1 if case.is_mla else 2) + (2 * case.Hkv * case.rope_dim * eb))
+    if case.int8:  # bf16 rows in; codes and one float32 scale per (token, head) out
+        stored = case.Hkv * (case.D + 4)
+        write = T * (4 + 2 * (row + stored))
+    else:
+        write = T * (4 + 2 * row * (1 if case.is_mla else 2) + (2 * case.Hkv * case.rope_dim * eb))
     if case.kind == "decode":
         lo = np.maximum(0, L - case.window) if case.window else np.zeros_like(L)
         keys = L - lo
@@ -94,6 +98,8 @@ def algorithmic_bytes(case):
         q_rows = case.q.shape[0] * case.H
     if case.is_mla:  # latent read once serves as key and value; rope part beside it
         kv = int(keys.sum()) * (case.D + case.rope_dim) * eb
+    elif case.int8:  # int8 codes plus a float32 scale per (key, head), K and V
+        kv = int(keys.sum()) * case.Hkv * 2 * (case.D + 4)
     else:
         kv = int(keys.sum()) * case.Hkv * 2 * case.D * eb
     qo = q_rows * (case.D + case.rope_dim) * eb + q_rows * case.D * eb
@@ -116,6 +122,8 @@ PROFILED = {
     "mla_mtp_decode": ("mla_decode_mla_mtp_decode.md", [_CSRC + "mla.hip"] + _COMMON),
     "mla_chunked_prefill": ("mla_decode_mla_chunked_prefill.md", [_CSRC + "mla.hip"] + _COMMON),
     "mla_latent_write": ("latent_write_mla_latent_write.md", [_CSRC + "latent_write.hip"] + _COMMON),
+    "mha_decode_7b_int8": ("decode_stream_mha_decode_7b_int8.md", _STREAM),
+    "gqa_decode_70b_int8": ("decode_stream_gqa_decode_70b_int8.md", _STREAM),
 }
 
 
@@ -163,6 +171,31 @@ def algorithmic_flops(case):
     return pairs * 2 * ((case.D + case.rope_dim) + case.D)
 
 
+def _int8_oracle_step(oracle, case):
+    """The oracle's step over an int8 cache: the pools are quantized and dequantized once
+    (the cache as it stands before the step); a step resolves the slots, quantizes the new
+    rows into them, refreshes their dequantized values and attends."""
+    from helpers import int8_state, oracle_slots, oracle_write_int8, to_f64
+    from oracle import int8_cache as q8
+
+    state = int8_state(case)
+    kc, ks, vc, vs = state
+    kd, vd = q8.dequantize_cache(kc, ks), q8.dequantize_cache(vc, vs)
+    q64 = to_f64(case.q, case.dtype)
+    bs = case.block_size
+
+    def step(units=None):
+        slots = oracle_slots(oracle, case)
+        oracle_write_int8(oracle, case, state, slots)
+        for sl in slots[slots >= 0]:
+            b, o = divmod(int(sl), bs)
+            kd[b, o] = q8.dequantize(kc[b, o], ks[b, :, o])
+            vd[b, o] = q8.dequantize(vc[b, o], vs[b, :, o])
+        oracle.paged_decode(q64, kd, vd, case.block_table, case.seq_lens, case.scale, case.window, units=units)
+
+    return step
+
+
 def cpu_baseline(case, target_s):
     """The oracle, as it stands, on the host cores.  Whole steps of the same workload
     when one fits the time target; otherwise one step whose attention covers a seeded
@@ -176,19 +209,24 @@ def cpu_baseline(case, target_s):
     rows = case.q.shape[0] * case.H
     rng = np.random.default_rng(0)
     pilot = np.sort(rng.choice(rows, size=min(rows, 256), replace=False))
+    if case.int8:
+        step = _int8_oracle_step(oracle, case)
+    else:
+        def step(units=None):
+            oracle_run(oracle, case, units=units, inplace=True)
     t0 = time.perf_counter()
-    oracle_run(oracle, case, units=pilot, inplace=True)
+    step(pilot)
     per_row = (time.perf_counter() - t0) / pilot.size
     r, w, a, _ = algorithmic_bytes(case)
     what = "output rows" if case.kind == "decode" else "query-row x head outputs"
     if per_row * rows <= target_s:
         t0 = time.perf_counter()
-        oracle_run(oracle, case, inplace=True)
+        step()
         one = time.perf_counter() - t0
         reps = max(1, int(target_s / max(one, 1e-3)))
         t0 = time.perf_counter()
         for _ in range(reps):
-            oracle_run(oracle, case, inplace=True)
+            step()
         el = (time.perf_counter() - t0) / reps
         sample = (f"{reps} whole steps (resolve + write + attention of all {rows} {what}) of "
                   f"{case.name} seed {case.seed_label}, {el * 1e3:.1f} ms per step")
@@ -196,7 +234,7 @@ def cpu_baseline(case, target_s):
         n = max(pilot.size, min(rows, int(target_s / per_row)))
         units = np.sort(rng.choice(rows, size=n, replace=False))
         t0 = time.perf_counter()
-        oracle_run(oracle, case, units=units, inplace=True)
+        step(units)
         el = (time.perf_counter() - t0) * rows / n
         sample = (f"one step of {case.name} seed {case.seed_label} with the attention of {n} of its "
                   f"{rows} {what} (seeded random sample), scaled by the row fraction to "
@@ -235,6 +273,26 @@ def cpu_baseline_latent(case, target_s):
     return {"value": round((r + w) / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole steps of {case.name} seed {case.seed_label} ({case.T} tokens), fp64 numpy, "
                       f"{el * 1e3:.1f} ms per step, 1 thread", "ms_per_step": round(el * 1e3, 3)}
+
+
+def int8_cache(torch, pkv, case):
+    """The workload's bf16 pools quantized into an int8 cache on the GPU by kv_cache_write
+    (set-up, before any timing; with a null block, block 0 keeps zero codes and NaN scales)."""
+    nb, bs, hkv, d = case.k_cache.shape
+    z8 = lambda: torch.zeros((nb, bs, hkv, d), dtype=torch.int8, device="cuda")  # noqa: E731
+    zs = lambda: torch.zeros((nb, hkv, bs), dtype=torch.float32, device="cuda")  # noqa: E731
+    cache = pkv.PagedKVCache(z8(), z8(), None, zs(), zs())
+    slots = torch.arange(nb * bs, dtype=torch.int32, device="cuda")
+    if case.null_block:
+        slots[:bs] = -1
+    pk, pv = _dev(torch, case.k_cache), _dev(torch, case.v_cache)
+    pkv.kv_cache_write(slots, pk.view(nb * bs, hkv, d), pv.view(nb * bs, hkv, d), cache)
+    if case.null_block:
+        cache.k_scale[0] = float("nan")
+        cache.v_scale[0] = float("nan")
+    torch.cuda.synchronize()
+    del pk, pv
+    return cache
 
 
 def run_latent(args, case, torch, pkv):
@@ -336,7 +394,10 @@ def main():
         run_latent(args, case, torch, pkv)
         return
     dev = lambda a: _dev(torch, a)  # noqa: E731
-    cache = pkv.PagedKVCache(dev(case.k_cache), dev(case.v_cache), dev(case.k_rope_cache))
+    if case.int8:
+        cache = int8_cache(torch, pkv, case)
+    else:
+        cache = pkv.PagedKVCache(dev(case.k_cache), dev(case.v_cache), dev(case.k_rope_cache))
     bt, sl = dev(case.block_table), dev(case.seq_lens)
     q, q_rope = dev(case.q), dev(case.q_rope)
     new_k, new_v, new_kr = dev(case.new_k), dev(case.new_v), dev(case.new_k_rope)
@@ -390,7 +451,8 @@ def main():
     result = _result(args, case, value, ms_step,
                      {"workload": case.name, "batch": case.B, "num_q_heads": case.H, "num_kv_heads": case.Hkv,
                       "head_dim": case.D, "rope_dim": case.rope_dim, "block_size": case.block_size,
-                      "window": case.window, "seq_len_total": int(case.seq_lens.sum()), "seed": args.seed})
+                      "window": case.window, "seq_len_total": int(case.seq_lens.sum()), "seed": args.seed,
+                      "cache": "int8 codes + float32 scale per (token, head)" if case.int8 else case.dtype})
     result.update({
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(case.new_pos.size / (ms_step * 1e-3), 1),

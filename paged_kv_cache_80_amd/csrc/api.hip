@@ -142,7 +142,7 @@ int32_t device_cu_count() {
 // The stream split needs a wave per KV head in every wave group.
 bool use_stream_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
   return !is_mla(c) && pkv::decode_mfma_supported(c->dtype, c->head_dim, p->num_q_heads / c->num_kv_heads) &&
-         c->num_kv_heads <= pkv::decode_stream_resident_waves(device_cu_count());
+         c->num_kv_heads <= pkv::decode_stream_resident_waves(device_cu_count(), c->dtype);
 }
 
 constexpr int32_t kMaxBpp = 1024;
@@ -162,7 +162,7 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
   DecodePlan plan{};
   if (use_stream_decode(p, c)) {
     plan.stream = true;
-    plan.resident_waves = pkv::decode_stream_resident_waves(device_cu_count());
+    plan.resident_waves = pkv::decode_stream_resident_waves(device_cu_count(), c->dtype);
     plan.split_tiles = p->split_tokens / 32;  // split_tokens is a multiple of the block size (>= 16)
     if (p->split_tokens > 0 && plan.split_tiles == 0) plan.split_tiles = 1;
     plan.max_np = 1;

@@ -69,7 +69,8 @@ constexpr int kD = 128;
 constexpr int kKeyTile = 32;
 constexpr int kTileLog2 = 5;
 constexpr int kRowBytes = kD * 2;                 // 256: one head row of K or V
-constexpr int kWaves = 4;                         // independent waves per workgroup
+constexpr int kWaves = 4;                         // independent waves per workgroup (bf16)
+constexpr int kWavesI8 = 8;                       // int8: half-size slots leave LDS for twice the waves
 constexpr float kRescaleLog2 = 8.f;
 
 // Tile geometry per cache type: bytes of one head row, of one tensor of a tile,
@@ -87,11 +88,18 @@ constexpr int kLdsPrefix = 2048;                   // batch + 1 up to this: pref
 // 16-byte chunk swizzles of row r in the staged K and V tiles.
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 7); }
-// int8 tiles (8 chunks per 128-byte row): K rows of one operand read (rows
-// 8 m + 4 u + e, m, e < 4) land in 8 distinct chunk positions per bank half; V
-// rows of one transposing read (8 consecutive rows) in 8 distinct positions.
-__device__ __forceinline__ int kswz8(int r) { return 2 * ((r >> 3) & 3) + ((r >> 1) & 1); }
-__device__ __forceinline__ int vswz8(int r) { return r & 7; }
+// int8 tiles (8 chunks per 128-byte row).  K operand rows of tile u are
+// r = 8 (l16 / 4) + 4 u + l16 % 4; with j = l16 = 4 (r / 8) + r % 4 the chunk
+// position is c ^ ((j / 2) ^ 4 (j % 2)): lanes 0..7 of a 16-byte read hit 8
+// distinct positions and lanes 0..15 distinct (row parity, position) pairs, so
+// the read is conflict-free with 8 or with 16 lanes served per cycle.  V rows
+// of a transposing read (8 consecutive rows, two such groups per half wave)
+// take position dt ^ (r % 8) ^ (r / 8 % 2).
+__device__ __forceinline__ int kswz8(int r) {
+  const int j = 4 * ((r >> 3) & 3) + (r & 3);
+  return (j >> 1) ^ ((j & 1) << 2);
+}
+__device__ __forceinline__ int vswz8(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Scalar (SMEM) load of a value that is uniform across the wave and read-only
 // for the whole kernel.  Vector loads retire in order, so a vector load of
@@ -161,13 +169,14 @@ struct Cursor {
 // column prefix (batch + 1 <= kLdsPrefix) and workgroup 0 also stores it for
 // the combine; otherwise tile_prefix_kernel has written it to the workspace.
 template <bool ONE_BLOCK, bool LDS_PREFIX, bool I8>
-__global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_stream_kernel(DecodeArgs a) {
   constexpr int KS = kD / 32;  // contraction steps of q.k
   constexpr int DT = kD / 16;  // 16-row tiles of O^T
+  constexpr int NW = I8 ? kWavesI8 : kWaves;
   using GT = Geo<I8>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_buf[kWaves * 2 * GT::kSlot];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_buf[NW * 2 * GT::kSlot];
   __shared__ int32_t s_prefix[LDS_PREFIX ? kLdsPrefix : 1];
-  __shared__ int32_t s_wave_sum[kWaves];
+  __shared__ int32_t s_wave_sum[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -181,7 +190,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
   if constexpr (LDS_PREFIX) {
     // Thread t owns sequences [kPerThread t, kPerThread (t + 1)): local sums,
     // a wave scan of the thread totals, then the waves' totals through LDS.
-    constexpr int kPerThread = kLdsPrefix / (kWaves * kWave);
+    constexpr int kPerThread = kLdsPrefix / (NW * kWave);
     int32_t incl[kPerThread];
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j)  // all loads first (clamped: B >= 1), then the sums
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
     if (tid == 0) s_prefix[0] = 0;
     __syncthreads();
     if (blockIdx.x == 0)
-      for (int i = tid; i <= B; i += kWaves * kWave) a.tile_prefix[i] = s_prefix[i];
+      for (int i = tid; i <= B; i += NW * kWave) a.tile_prefix[i] = s_prefix[i];
   }
   // prefix[i]: columns of the sequences before i (prefix[B] = all columns).
   auto prefix_at = [&](int i) -> int32_t {
@@ -219,8 +228,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
   };
 
   const int64_t C = prefix_at(B);
-  const int64_t NG = stream_groups(C, gridDim.x * kWaves, Hkv, a.split_tiles);
-  const int64_t w = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t NG = stream_groups(C, gridDim.x * NW, Hkv, a.split_tiles);
+  const int64_t w = (int64_t)blockIdx.x * NW + wave;
   const int64_t grp = w / Hkv;  // wave-uniform
   const int g = (int)(w - grp * Hkv);
   if (grp >= NG) return;
@@ -289,18 +298,22 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
   // K operand (tile u, step ks): row 8(l16/4) + 4u + l16%4, bytes 32ks + 8lg.
   // V^T operand of dim tile dt: the transposing read of row 8lg + l16/2, half
   // l16 % 2 of logical chunk dt.
-  uint32_t k_src8[4], v_src8 = 0;
-  int kr8_off[2][KS], vr8_off[DT];
+  // The contraction order of q.k is permuted for int8: step ks of lane group lg
+  // takes dims 16 (lg + 4 (ks / 2)) + 8 (ks % 2) .. + 8, so one 16-byte read of
+  // chunk lg (or lg + 4) of a K row feeds two steps.
+  uint32_t k_src8[4], v_src8[2] = {0, 0};
+  int kr8_off[2][2], vr8_off[DT];
   if constexpr (I8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) k_src8[i] = 16 * ((lane & 7) ^ kswz8(8 * i + (lane >> 3)));
-    v_src8 = 16 * ((lane & 7) ^ vswz8(lane >> 3));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v_src8[i] = 16 * ((lane & 7) ^ vswz8(8 * i + (lane >> 3)));
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int h = 0; h < 2; ++h) {
         const int r = 8 * (l16 >> 2) + 4 * u + (l16 & 3);
-        kr8_off[u][ks] = r * GT::kRow + 16 * ((2 * ks + (lg >> 1)) ^ kswz8(r)) + 8 * (lg & 1);
+        kr8_off[u][h] = r * GT::kRow + 16 * ((lg + 4 * h) ^ kswz8(r));
       }
     const int rv = 8 * lg + (l16 >> 1);
 #pragma unroll
@@ -342,7 +355,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t row = (uint32_t)min(max(8 * i + (lane >> 3), lo_r), hi_r) * row_bytes;
-          load_lds16_s(vb, row + v_src8, vdst + 1024 * i);
+          load_lds16_s(vb, row + v_src8[i & 1], vdst + 1024 * i);
         }
         if (lane < 16)
           load_lds16(scale_src + ((((int64_t)phys * Hkv + g) << bs_log2) + (t0 & bs_mask) + key), sdst);
@@ -355,7 +368,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
           const int32_t phys = (j >> bs_log2) == blk ? e0 : e1;
           const int64_t slot = ((int64_t)phys << bs_log2) + (j & bs_mask);
           load_lds16(kcache8 + slot * row_bytes + head_off + k_src8[i], kdst + 1024 * i);
-          load_lds16(vcache8 + slot * row_bytes + head_off + v_src8, vdst + 1024 * i);
+          load_lds16(vcache8 + slot * row_bytes + head_off + v_src8[i & 1], vdst + 1024 * i);
         }
         if (lane < 16) {
           const int j = t0 + key;  // the lane's 4 keys lie in one 16-key block
@@ -403,8 +416,10 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
   auto load_q = [&](const Cursor& c) {
     const int64_t qrow = (int64_t)c.b * H + (int64_t)g * G + l16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = cvalid ? ld16(qp + qrow * kD + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = I8 ? 16 * (lg + 4 * (ks >> 1)) + 8 * (ks & 1) : 32 * ks + 8 * lg;
+      qf[ks] = cvalid ? ld16(qp + qrow * kD + d0) : make_uint4(0, 0, 0, 0);
+    }
   };
 
   f32x4_t o[DT];
@@ -444,9 +459,10 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void decode_stream_kernel(Decode
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 af = i8x8_to_bf16(*reinterpret_cast<const uint2*>(kt + kr8_off[u][ks]));
-        s[u] = mfma_bf16(af, qf[ks], ks == 0 ? f32x4_zero() : s[u]);
+      for (int h = 0; h < 2; ++h) {
+        const uint4 kw = *reinterpret_cast<const uint4*>(kt + kr8_off[u][h]);
+        s[u] = mfma_bf16(i8x8_to_bf16(make_uint2(kw.x, kw.y)), qf[2 * h], h == 0 ? f32x4_zero() : s[u]);
+        s[u] = mfma_bf16(i8x8_to_bf16(make_uint2(kw.z, kw.w)), qf[2 * h + 1], s[u]);
       }
     }
     // Lane (n, lg) holds keys 8 lg + 4 u + e of tile u.
@@ -682,7 +698,9 @@ bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
   return (dtype == PKV_BF16 || dtype == PKV_INT8) && head_dim == kD && group >= 1 && group <= 16;
 }
 
-int32_t decode_stream_resident_waves(int32_t cu_count) { return cu_count * kWaves; }
+int32_t decode_stream_resident_waves(int32_t cu_count, int32_t dtype) {
+  return cu_count * (dtype == PKV_INT8 ? kWavesI8 : kWaves);
+}
 
 size_t decode_stream_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t resident_waves,
                                size_t* ws_o_offset, size_t* ws_ml_offset) {
@@ -703,15 +721,17 @@ hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const unsigned grid = (unsigned)(a.resident_waves / kWaves);
   const bool one_block = a.block_size_log2 >= kTileLog2;
-  const dim3 blk(kWaves * kWave);
   if (a.dtype == PKV_INT8) {
+    const unsigned grid = (unsigned)(a.resident_waves / kWavesI8);
+    const dim3 blk(kWavesI8 * kWave);
     if (lds_prefix && one_block) decode_stream_kernel<true, true, true><<<grid, blk, 0, stream>>>(a);
     else if (lds_prefix) decode_stream_kernel<false, true, true><<<grid, blk, 0, stream>>>(a);
     else if (one_block) decode_stream_kernel<true, false, true><<<grid, blk, 0, stream>>>(a);
     else decode_stream_kernel<false, false, true><<<grid, blk, 0, stream>>>(a);
   } else {
+    const unsigned grid = (unsigned)(a.resident_waves / kWaves);
+    const dim3 blk(kWaves * kWave);
     if (lds_prefix && one_block) decode_stream_kernel<true, true, false><<<grid, blk, 0, stream>>>(a);
     else if (lds_prefix) decode_stream_kernel<false, true, false><<<grid, blk, 0, stream>>>(a);
     else if (one_block) decode_stream_kernel<true, false, false><<<grid, blk, 0, stream>>>(a);

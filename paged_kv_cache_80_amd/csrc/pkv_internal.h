@@ -89,7 +89,7 @@ bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);
 // bf16 or int8 caches, head_dim 128, head groups up to 16.  Launches the tile scan, the decode
 // and the piece combine.
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
-int32_t decode_stream_resident_waves(int32_t cu_count);
+int32_t decode_stream_resident_waves(int32_t cu_count, int32_t dtype);
 size_t decode_stream_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t resident_waves,
                                size_t* ws_o_offset, size_t* ws_ml_offset);
 hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream);
