@@ -371,8 +371,8 @@ def _result(args, case, value, ms_step, config):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this build "
-              "(sharding is described in DESIGN.md, not run)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path runs "
+              "unsharded on one device", file=sys.stderr)
         sys.exit(2)
     import torch
 
