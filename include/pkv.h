@@ -18,7 +18,9 @@
  *     batch_idx, pos) are int32 (the skill page's notes require an int32
  *     block table).
  *   - Element arrays are float32 or bfloat16, one dtype per call; there is no
- *     implicit conversion.  Every element base pointer must be 16-byte aligned.
+ *     implicit conversion.  The one exception is an int8 cache (PKV_INT8),
+ *     whose codes and float32 scales go with bf16 queries, rows and outputs.
+ *     Every element base pointer must be 16-byte aligned.
  *   - Only host-visible arguments are validated (pointers, sizes, shapes,
  *     dtypes, scale, workspace size).  A failed check returns a non-zero
  *     status, launches nothing and leaves a message for pkv_last_error().
