@@ -125,6 +125,13 @@ def _check_elems(cache: "PagedKVCache", *ts) -> None:
             raise TypeError(f"expected {want} rows for a {cache.k_cache.dtype} cache, got {t.dtype}")
 
 
+def _expect(t: Optional[torch.Tensor], shape: tuple, name: str) -> None:
+    """The kernels read exactly these extents through plain pointers: a smaller tensor would be
+    read past its end, so a mismatch is refused here."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _stream(stream) -> Optional[int]:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -164,6 +171,10 @@ def pkv_resolve_slots(block_table: torch.Tensor, block_size: int, batch_idx: tor
     """slot = block_table[b, pos // block_size] * block_size + pos % block_size (int32; pos < 0 -> -1)."""
     bt = _i32(block_table)
     n = batch_idx.numel()
+    if bt.dim() != 2:
+        raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+    _expect(pos, (n,), "pos")
+    _expect(slots_out, (n,), "slots_out")
     if slots_out is None:
         slots_out = torch.empty(n, dtype=torch.int32, device=bt.device)
     _check(load().pkv_resolve_slots(_ptr(bt), bt.shape[0], bt.shape[1], block_size,
@@ -174,9 +185,16 @@ def pkv_resolve_slots(block_table: torch.Tensor, block_size: int, batch_idx: tor
 
 def kv_cache_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor],
                    cache: PagedKVCache, k_rope: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Copy row t of k (v, k_rope) to cache row slot_mapping[t] (negative slots skip)."""
-    d = cache.desc()
+    """Copy row t of k (v, k_rope) to cache row slot_mapping[t] (negative slots skip); an int8 cache
+    quantizes the bf16 rows instead."""
+    n = slot_mapping.numel()
+    _, _, hkv, hd = cache.k_cache.shape
+    _expect(k, (n, hkv, hd), "k")
+    _expect(v, (n, hkv, hd), "v")
+    if k_rope is not None:
+        _expect(k_rope, (n, hkv, cache.k_rope_cache.shape[3]), "k_rope")
     _check_elems(cache, k, v, k_rope)
+    d = cache.desc()
     _check(load().kv_cache_write(_ptr(_i32(slot_mapping)), slot_mapping.numel(), _ptr(k), _ptr(v),
                                  _ptr(k_rope), ctypes.byref(d), _stream(stream)))
 
@@ -187,16 +205,31 @@ def kv_rmsnorm_rope_cache(latent: torch.Tensor, gamma: torch.Tensor, cos: torch.
                           k_rope_out: Optional[torch.Tensor] = None, stream=None) -> None:
     """RMSNorm(latent[:, :512]) * gamma and RoPE(latent[:, 512:]; cos, sin) into the MLA cache rows
     slot_mapping[t] (negative slots skip), and into k_nope_out / k_rope_out when given."""
-    d = cache.desc()
     n = slot_mapping.numel()
-    if latent.shape[0] != n or cos.shape[0] != n or sin.shape[0] != n:
-        raise ValueError("latent, cos, sin and slot_mapping must have one row per token")
+    _expect(latent, (n, 576), "latent")
+    _expect(gamma, (512,), "gamma")
+    _expect(cos, (n, 64), "cos")
+    _expect(sin, (n, 64), "sin")
+    _expect(k_nope_out, (n, 512), "k_nope_out")
+    _expect(k_rope_out, (n, 64), "k_rope_out")
+    d = cache.desc()
     for t in (latent, gamma, cos, sin, k_nope_out, k_rope_out):
         if t is not None and t.dtype != cache.k_cache.dtype:
             raise TypeError("every array must have the cache dtype")
     _check(load().kv_rmsnorm_rope_cache(_ptr(latent), _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(_i32(slot_mapping)), n,
                                         float(eps), rope_layout, ctypes.byref(d), _ptr(k_nope_out), _ptr(k_rope_out),
                                         _stream(stream)))
+
+
+def _check_attn_shapes(cache: PagedKVCache, q, q_rope, block_table, batch: int, out) -> None:
+    rows, H, D = q.shape
+    if D != cache.k_cache.shape[3]:
+        raise ValueError(f"q head_dim {D} differs from the cache's {cache.k_cache.shape[3]}")
+    if q_rope is not None and cache.k_rope_cache is not None:
+        _expect(q_rope, (rows, H, cache.k_rope_cache.shape[3]), "q_rope")
+    if block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError(f"block_table must be [{batch}, max_blocks_per_seq], got {tuple(block_table.shape)}")
+    _expect(out, (rows, H, D), "out")
 
 
 def _params(batch, num_q_heads, block_table, scale, window, out_dtype, split_tokens) -> AttnParams:
@@ -218,6 +251,8 @@ def paged_attn_decode(q: torch.Tensor, cache: PagedKVCache, block_table: torch.T
                       workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """q [B, H, D] -> out [B, H, D]; seq_lens counts keys including this step's token."""
     B, H, D = q.shape
+    _check_attn_shapes(cache, q, q_rope, block_table, B, out)
+    _expect(seq_lens, (B,), "seq_lens")
     _check_elems(cache, q, q_rope)
     if out is None:
         out = torch.empty((B, H, D), dtype=out_dtype or q.dtype, device=q.device)
@@ -242,6 +277,8 @@ def paged_attn_prefill(q: torch.Tensor, cache: PagedKVCache, block_table: torch.
     """q TND [T, H, D] -> out [T, H, D], bottom-right causal over each sequence's keys."""
     T, H, D = q.shape
     B = cu_seqlens_q.numel() - 1
+    _check_attn_shapes(cache, q, q_rope, block_table, B, out)
+    _expect(seq_lens_kv, (B,), "seq_lens_kv")
     _check_elems(cache, q, q_rope)
     if out is None:
         out = torch.empty((T, H, D), dtype=out_dtype or q.dtype, device=q.device)

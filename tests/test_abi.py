@@ -148,3 +148,41 @@ def test_resolve_rejects_malformed_arguments(lib):
 
 def test_empty_batch_is_a_no_op(lib):
     assert _decode(lib, _cache(), _params(batch=0)) == 0
+
+
+def test_binding_refuses_mismatched_shapes():
+    """The kernels read fixed extents through plain pointers; the binding refuses tensors whose
+    shapes would let them read past an end (checked before any device pointer is taken)."""
+    torch = pytest.importorskip("torch")
+    import paged_kv_cache_80_amd as pkv
+
+    kc = torch.zeros((4, 16, 2, 128), dtype=torch.bfloat16)
+    cache = pkv.PagedKVCache(kc, kc.clone())
+    q = torch.zeros((3, 4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="block_table"):
+        pkv.paged_attn_decode(q, cache, torch.zeros((2, 4), dtype=torch.int32),
+                              torch.ones(3, dtype=torch.int32), 0.1)
+    with pytest.raises(ValueError, match="seq_lens"):
+        pkv.paged_attn_decode(q, cache, torch.zeros((3, 4), dtype=torch.int32),
+                              torch.ones(2, dtype=torch.int32), 0.1)
+    with pytest.raises(ValueError, match="head_dim"):
+        pkv.paged_attn_decode(q[..., :64], cache, torch.zeros((3, 4), dtype=torch.int32),
+                              torch.ones(3, dtype=torch.int32), 0.1)
+    with pytest.raises(ValueError, match="out"):
+        pkv.paged_attn_decode(q, cache, torch.zeros((3, 4), dtype=torch.int32), torch.ones(3, dtype=torch.int32),
+                              0.1, out=torch.zeros((3, 4, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="k has shape"):
+        pkv.kv_cache_write(torch.zeros(5, dtype=torch.int32), torch.zeros((4, 2, 128), dtype=torch.bfloat16),
+                           torch.zeros((5, 2, 128), dtype=torch.bfloat16), cache)
+    with pytest.raises(ValueError, match="seq_lens_kv"):
+        pkv.paged_attn_prefill(q, cache, torch.zeros((2, 4), dtype=torch.int32),
+                               torch.tensor([0, 1, 3], dtype=torch.int32), torch.ones(3, dtype=torch.int32), 2, 0.1)
+    with pytest.raises(ValueError, match="pos"):
+        pkv.pkv_resolve_slots(torch.zeros((2, 4), dtype=torch.int32), 16, torch.zeros(3, dtype=torch.int32),
+                              torch.zeros(2, dtype=torch.int32))
+    lat_cache = pkv.PagedKVCache(torch.zeros((4, 16, 1, 512), dtype=torch.bfloat16), None,
+                                 torch.zeros((4, 16, 1, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="cos"):
+        pkv.kv_rmsnorm_rope_cache(torch.zeros((3, 576), dtype=torch.bfloat16), torch.zeros(512, dtype=torch.bfloat16),
+                                  torch.zeros((2, 64), dtype=torch.bfloat16), torch.zeros((3, 64), dtype=torch.bfloat16),
+                                  torch.zeros(3, dtype=torch.int32), 1e-6, lat_cache)
