@@ -120,12 +120,14 @@ __device__ __forceinline__ int32_t seq_tiles(int32_t L, int32_t window) {
 }
 
 // Wave groups that share the C columns: every resident group, or fewer when a
-// target number of tiles per wave is given (split_tiles > 0).
+// target number of tiles per wave is given (split_tiles > 0), and never more
+// groups than columns (a group without a column would only leave an empty slot
+// for the combine to skip).
 __device__ __forceinline__ int64_t stream_groups(int64_t C, int32_t resident_waves, int32_t Hkv,
                                                  int32_t split_tiles) {
   int64_t ng = resident_waves / Hkv;  // >= 1: the host checks H_kv <= resident waves
   if (split_tiles > 0) ng = min(ng, max<int64_t>(1, (C + split_tiles - 1) / split_tiles));
-  return ng;
+  return max<int64_t>(1, min(ng, C));
 }
 // The group whose run [C x / NG, C (x+1) / NG) holds column t.
 __device__ __forceinline__ int64_t group_of_column(int64_t t, int64_t C, int64_t ng) {
