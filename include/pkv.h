@@ -67,7 +67,10 @@ typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_INT8 = 2 } pkv_dtype;
  * q = round_half_even(x * (127 / max|x|)) (float32 arithmetic; an all-zero row has
  * s = 0, q = 0) and stands for q * s.  Queries, new rows and outputs stay bf16.
  * Standard attention only (no rope part), head_dim 128; kv_cache_write quantizes,
- * paged_attn_decode reads it (head groups up to 16); prefill does not take it. */
+ * paged_attn_decode reads it (head groups up to 16); prefill does not take it.
+ *
+ * Every cache: a slot row (num_kv_heads * head_dim elements, and the rope row)
+ * is a multiple of 16 bytes and at most 16 MiB; else PKV_ERR_UNSUPPORTED. */
 typedef struct {
   void* k_cache;
   void* v_cache;

@@ -66,6 +66,10 @@ pkv_status check_cache(const pkv_paged_cache* c) {
     return fail(PKV_ERR_INVALID_ARG, "k_rope_cache must be given exactly when rope_dim > 0");
   const int64_t row = (int64_t)c->num_kv_heads * c->head_dim * elem_bytes(c->dtype);
   if (row % 16 != 0) return fail(PKV_ERR_UNSUPPORTED, "a cache row of %lld bytes is not a multiple of 16", (long long)row);
+  // Row byte counts travel as 32-bit values and tile loads address up to 64 slot
+  // rows from one base with 32-bit lane offsets.
+  if (row > (int64_t(1) << 24))
+    return fail(PKV_ERR_UNSUPPORTED, "a cache row of %lld bytes exceeds 16 MiB", (long long)row);
   if (c->rope_dim > 0 && ((int64_t)c->num_kv_heads * c->rope_dim * elem_bytes(c->dtype)) % 16 != 0)
     return fail(PKV_ERR_UNSUPPORTED, "a rope row is not a multiple of 16 bytes");
   if (!aligned16(c->k_cache) || !aligned16(c->v_cache) || (c->k_rope_cache && !aligned16(c->k_rope_cache)))
@@ -490,9 +494,6 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
   if (!pkv::prefill_mfma_supported(cache->dtype, cache->head_dim))
     return fail(PKV_ERR_UNSUPPORTED, "prefill: needs bf16 and head_dim 64 or 128 (got dtype %d, head_dim %d)",
                 cache->dtype, cache->head_dim);
-  // Tile loads address up to 64 slot rows from one base with 32-bit lane offsets.
-  if ((int64_t)cache->num_kv_heads * cache->head_dim * 2 > (int64_t(1) << 24))
-    return fail(PKV_ERR_UNSUPPORTED, "prefill: slot rows beyond 16 MiB (num_kv_heads %d)", cache->num_kv_heads);
   pkv::PrefillArgs a{};
   a.q = q;
   a.k_cache = cache->k_cache;

@@ -75,6 +75,7 @@ def _decode(lib, cache, params, q=FAKE, q_rope=None, out=FAKE, ws=None, ws_bytes
     ({"block_size": 96}, {}, 2, "block_size"),
     ({"num_blocks": 0}, {}, 1, "num_blocks"),
     ({"k_cache": FAKE + 2}, {}, 1, "aligned"),
+    ({"num_kv_heads": 65536, "head_dim": 256, "dtype": pkv.PKV_F32}, {"num_q_heads": 65536}, 2, "16 MiB"),
     ({"rope_dim": 64}, {}, 1, "k_rope_cache"),
     # MLA constraints of the skill page's mode 3
     ({"rope_dim": 64, "k_rope_cache": FAKE + 0x2000, "num_kv_heads": 1, "head_dim": 512}, {}, 1, "alias"),
