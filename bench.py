@@ -29,6 +29,12 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, published
+# Cold-cache timing: the timed steps rotate over copies of the step's bulk data
+# (the paged cache; for the fused write also its inputs and outputs) until the
+# copies together hold at least this much, so that no step finds its bytes in
+# the 256 MB last-level cache (MALL) from the step before.  The warm figure (one
+# copy, the same bytes every step) is reported beside it.
+COLD_SET_BYTES = 2 << 30
 METRIC = "paged decode KV GB/s (% of HBM peak) + tokens/s; prefill MFMA util"
 
 
@@ -41,6 +47,9 @@ def parse_args():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split-tokens", type=int, default=0, help="decode partition size (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="time the cold-cache steps only (no warm pass, no copy reference), so that a profiler's "
+                         "per-kernel averages cover exactly the reported steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device copy of this many MiB (the reference "
@@ -48,7 +57,8 @@ def parse_args():
     return ap.parse_args()
 
 
-def copy_calibration(torch, mib, steps):
+def time_copy(torch, mib, steps):
+    """A plain device copy of `mib` MiB: (ms per copy, read + written bytes per second in GB/s)."""
     n = mib << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -62,8 +72,34 @@ def copy_calibration(torch, mib, steps):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    del src, dst
+    torch.cuda.empty_cache()
+    return ms, 2 * n / (ms * 1e-3) / 1e9
+
+
+def copy_calibration(torch, mib, steps):
+    ms, gbs = time_copy(torch, mib, steps)
+    n = mib << 20
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms_per_copy": round(ms, 4),
-                      "copy_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+                      "copy_GBps": round(gbs, 1)}), flush=True)
+
+
+def stream_copy_reference(torch):
+    """What a plain streaming copy reaches on this GPU in the same run (1 GiB, read +
+    written bytes): the achievable-bandwidth reference beside the 8 TB/s datasheet peak."""
+    ms, gbs = time_copy(torch, 1024, 10)
+    return {"GBps": round(gbs, 1), "ms": round(ms, 4), "bytes": 2 << 30, "what": "torch device copy of 1 GiB"}
+
+
+def _nbytes(*ts):
+    return sum(t.numel() * t.element_size() for t in ts if t is not None)
+
+
+def _copies(make, set_bytes):
+    """[original, copy, ...]: enough copies of a set of `set_bytes` bytes that together they
+    hold at least COLD_SET_BYTES; make(0) is the original, make(i > 0) a fresh copy."""
+    n = max(1, -(-COLD_SET_BYTES // max(int(set_bytes), 1)))
+    return [make(i) for i in range(n)]
 
 
 def _dev(torch, a):
@@ -196,6 +232,18 @@ def _int8_oracle_step(oracle, case):
     return step
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), for the record beside a CPU figure."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, target_s):
     """The oracle, as it stands, on the host cores.  Whole steps of the same workload
     when one fits the time target; otherwise one step whose attention covers a seeded
@@ -240,7 +288,7 @@ def cpu_baseline(case, target_s):
                   f"{rows} {what} (seeded random sample), scaled by the row fraction to "
                   f"{el * 1e3:.1f} ms per step")
     return {"value": round((r + w + a) / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{sample}, fp64, {threads} threads", "ms_per_step": round(el * 1e3, 3)}
+            "sample": f"{sample}, fp64, {threads} threads", "ms_per_step": round(el * 1e3, 3), "cpu": cpu_model()}
 
 
 def latent_bytes(case):
@@ -272,7 +320,7 @@ def cpu_baseline_latent(case, target_s):
     r, w = latent_bytes(case)
     return {"value": round((r + w) / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole steps of {case.name} seed {case.seed_label} ({case.T} tokens), fp64 numpy, "
-                      f"{el * 1e3:.1f} ms per step, 1 thread", "ms_per_step": round(el * 1e3, 3)}
+                      f"{el * 1e3:.1f} ms per step, 1 thread", "ms_per_step": round(el * 1e3, 3), "cpu": cpu_model()}
 
 
 def int8_cache(torch, pkv, case):
@@ -306,16 +354,23 @@ def run_latent(args, case, torch, pkv):
     kn = torch.empty((case.T, 512), dtype=tdt, device="cuda") if case.outputs else None
     kr = torch.empty((case.T, 64), dtype=tdt, device="cuda") if case.outputs else None
 
-    def step(e0=None, e1=None):
+    # the bulk data of one step: inputs read, cache and returned rows written
+    bulk = (lat, cos, sin, cache.k_cache, cache.k_rope_cache, kn, kr)
+    cl = lambda t: None if t is None else t.clone()  # noqa: E731
+    sets = _copies(lambda i: bulk if i == 0 else tuple(cl(t) for t in bulk), _nbytes(*bulk))
+
+    def step(i, e0=None, e1=None):
+        l_, c_, s_, cn, cr, kn_, kr_ = sets[i % len(sets)]
         pkv.pkv_resolve_slots(bt, case.block_size, bidx, pos, slots_out=slots)
         if e0 is not None:
             e0.record()
-        pkv.kv_rmsnorm_rope_cache(lat, gamma, cos, sin, slots, case.eps, cache, rope_layout=case.layout,
-                                  k_nope_out=kn, k_rope_out=kr)
+        pkv.kv_rmsnorm_rope_cache(l_, gamma, c_, s_, slots, case.eps, pkv.PagedKVCache(cn, None, cr),
+                                  rope_layout=case.layout, k_nope_out=kn_, k_rope_out=kr_)
         if e1 is not None:
             e1.record()
 
     ms_step, ms_k = _timed(torch, step, args)
+    warm = None if args.cold_only else _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), args)
     r_b, w_b = latent_bytes(case)
     value = (r_b + w_b) / (ms_step * 1e-3) / 1e9
     k_gbs = w_b / (ms_k * 1e-3) / 1e9
@@ -324,7 +379,12 @@ def run_latent(args, case, torch, pkv):
                                                   "rope_layout": "half" if case.layout == 0 else "interleaved",
                                                   "returned_rows": case.outputs, "seed": args.seed})
     result.update({"hbm_frac": round(value / HBM_PEAK_GBS, 4), "tokens_per_s": round(case.T / (ms_step * 1e-3), 1),
-                   "kernel_ms": round(ms_k, 4), "kernel_GBps": round(k_gbs, 2)})
+                   "kernel_ms": round(ms_k, 4), "kernel_GBps": round(k_gbs, 2),
+                   "cold_cache": {"copies": len(sets), "bytes_per_copy": _nbytes(*bulk)}})
+    if warm is not None:
+        result["warm"] = {"ms_per_step": round(warm[0], 4), "kernel_ms": round(warm[1], 4),
+                          "kernel_GBps": round(w_b / (warm[1] * 1e-3) / 1e9, 2)}
+        result["stream_copy"] = stream_copy_reference(torch)
     result["roofline"] = {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(args.workload),
                           "kernel": "kv_rmsnorm_rope_cache", "bytes_per_launch": w_b}
@@ -335,16 +395,16 @@ def run_latent(args, case, torch, pkv):
 
 def _timed(torch, step, args):
     """W untimed steps, then K timed steps between synchronisations; returns (ms per step,
-    mean ms between each step's two events)."""
-    for _ in range(args.warmup):
-        step()
+    mean ms between each step's two events).  step(i, e0, e1) runs step number i."""
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for e0, e1 in ev:
-        step(e0, e1)
+    for i, (e0, e1) in enumerate(ev):
+        step(args.warmup + i, e0, e1)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / args.steps, float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
@@ -414,24 +474,32 @@ def main():
     max_q = int(np.diff(case.cu_seqlens_q).max(initial=0)) if case.kind == "prefill" else 1
     cu = dev(case.cu_seqlens_q)
 
-    def attend():
+    def attend(c):
         if case.kind == "decode":
-            pkv.paged_attn_decode(q, cache, bt, sl, case.scale, case.window, q_rope=q_rope, out=out,
+            pkv.paged_attn_decode(q, c, bt, sl, case.scale, case.window, q_rope=q_rope, out=out,
                                   split_tokens=args.split_tokens, workspace=ws)
         else:
-            pkv.paged_attn_prefill(q, cache, bt, cu, sl, max_q, case.scale, case.window, q_rope=q_rope,
+            pkv.paged_attn_prefill(q, c, bt, cu, sl, max_q, case.scale, case.window, q_rope=q_rope,
                                    out=out, workspace=ws)
 
-    def step(e0=None, e1=None):
+    cache_bytes = _nbytes(cache.k_cache, cache.v_cache, cache.k_rope_cache, cache.k_scale, cache.v_scale)
+    cl = lambda t: None if t is None else t.clone()  # noqa: E731
+    caches = _copies(lambda i: cache if i == 0 else pkv.PagedKVCache(cl(cache.k_cache), cl(cache.v_cache),
+                                                                      cl(cache.k_rope_cache), cl(cache.k_scale),
+                                                                      cl(cache.v_scale)), cache_bytes)
+
+    def step(i, e0=None, e1=None):
+        c = caches[i % len(caches)]
         pkv.pkv_resolve_slots(bt, case.block_size, bidx, pos, slots_out=slots)
-        pkv.kv_cache_write(slots, new_k, new_v, cache, k_rope=new_kr)
+        pkv.kv_cache_write(slots, new_k, new_v, c, k_rope=new_kr)
         if e0 is not None:
             e0.record()
-        attend()
+        attend(c)
         if e1 is not None:
             e1.record()
 
     ms_step, ms_attn = _timed(torch, step, args)
+    warm = None if args.cold_only else _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), args)
 
     r_b, w_b, a_b, kv_b = algorithmic_bytes(case)
     flops = algorithmic_flops(case)
@@ -460,7 +528,13 @@ def main():
         "attention_GBps": round(attn_gbs, 2),
         "mfma_util": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roofline,
+        "cold_cache": {"copies": len(caches), "bytes_per_copy": cache_bytes},
     })
+    if warm is not None:
+        result["warm"] = {"ms_per_step": round(warm[0], 4), "attention_ms": round(warm[1], 4),
+                          "attention_GBps": round(a_b / (warm[1] * 1e-3) / 1e9, 2),
+                          "mfma_util": round(flops / (warm[1] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        result["stream_copy"] = stream_copy_reference(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(result), flush=True)
