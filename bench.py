@@ -287,8 +287,19 @@ def cpu_baseline(case, target_s):
         sample = (f"one step of {case.name} seed {case.seed_label} with the attention of {n} of its "
                   f"{rows} {what} (seeded random sample), scaled by the row fraction to "
                   f"{el * 1e3:.1f} ms per step")
-    return {"value": round((r + w + a) / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{sample}, fp64, {threads} threads", "ms_per_step": round(el * 1e3, 3), "cpu": cpu_model()}
+    res = {"value": round((r + w + a) / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{sample}, fp64, {threads} threads", "ms_per_step": round(el * 1e3, 3), "cpu": cpu_model()}
+    if case.name in ("tiny_f32_decode", "mha_decode_7b") and not case.int8:
+        # The same oracle on one thread: a seeded sample of rows, scaled to the whole step.
+        n1 = min(rows, 64)
+        units1 = np.sort(np.random.default_rng(1).choice(rows, size=n1, replace=False))
+        t0 = time.perf_counter()
+        oracle_run(oracle, case, units=units1, inplace=True, nthreads=1)
+        el1 = (time.perf_counter() - t0) * rows / n1
+        res["one_thread"] = {"value": round((r + w + a) / el1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                             "sample": f"the attention of {n1} of the {rows} {what} on one thread, scaled by the "
+                                       f"row fraction to {el1 * 1e3:.1f} ms per step"}
+    return res
 
 
 def latent_bytes(case):
