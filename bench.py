@@ -380,7 +380,7 @@ def run_latent(args, case, torch, pkv):
         if e1 is not None:
             e1.record()
 
-    ms_step, ms_k = _timed(torch, step, args)
+    ms_step, ms_k, med_k = _timed(torch, step, args)
     warm = None if args.cold_only else _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), args)
     r_b, w_b = latent_bytes(case)
     value = (r_b + w_b) / (ms_step * 1e-3) / 1e9
@@ -390,7 +390,7 @@ def run_latent(args, case, torch, pkv):
                                                   "rope_layout": "half" if case.layout == 0 else "interleaved",
                                                   "returned_rows": case.outputs, "seed": args.seed})
     result.update({"hbm_frac": round(value / HBM_PEAK_GBS, 4), "tokens_per_s": round(case.T / (ms_step * 1e-3), 1),
-                   "kernel_ms": round(ms_k, 4), "kernel_GBps": round(k_gbs, 2),
+                   "kernel_ms": round(ms_k, 4), "kernel_ms_median": round(med_k, 4), "kernel_GBps": round(k_gbs, 2),
                    "cold_cache": {"copies": len(sets), "bytes_per_copy": _nbytes(*bulk)}})
     if warm is not None:
         result["warm"] = {"ms_per_step": round(warm[0], 4), "kernel_ms": round(warm[1], 4),
@@ -406,7 +406,8 @@ def run_latent(args, case, torch, pkv):
 
 def _timed(torch, step, args):
     """W untimed steps, then K timed steps between synchronisations; returns (ms per step,
-    mean ms between each step's two events).  step(i, e0, e1) runs step number i."""
+    mean ms between each step's two events, their median).  step(i, e0, e1) runs step
+    number i."""
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -418,7 +419,8 @@ def _timed(torch, step, args):
         step(args.warmup + i, e0, e1)
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / args.steps, float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    per = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return start.elapsed_time(end) / args.steps, float(np.mean(per)), float(np.median(per))
 
 
 def _result(args, case, value, ms_step, config):
@@ -509,7 +511,7 @@ def main():
         if e1 is not None:
             e1.record()
 
-    ms_step, ms_attn = _timed(torch, step, args)
+    ms_step, ms_attn, med_attn = _timed(torch, step, args)
     warm = None if args.cold_only else _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), args)
 
     r_b, w_b, a_b, kv_b = algorithmic_bytes(case)
@@ -536,6 +538,7 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(case.new_pos.size / (ms_step * 1e-3), 1),
         "attention_ms": round(ms_attn, 4),
+        "attention_ms_median": round(med_attn, 4),
         "attention_GBps": round(attn_gbs, 2),
         "mfma_util": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roofline,
