@@ -154,6 +154,7 @@ PROFILED = {
     "gqa_decode_70b": ("decode_stream_gqa_decode_70b.md", _STREAM),
     "gqa_decode_70b_window4096": ("decode_stream_gqa_decode_70b_window4096.md", _STREAM),
     "chunked_prefill": ("prefill_mfma_chunked_prefill.md", [_CSRC + "prefill.hip"] + _COMMON),
+    "gqa_mtp_decode": ("prefill_mfma_gqa_mtp_decode.md", [_CSRC + "prefill.hip"] + _COMMON),
     "mla_decode": ("mla_decode_mla_decode.md", [_CSRC + "mla.hip", _CSRC + "decode.hip"] + _COMMON),
     "mla_mtp_decode": ("mla_decode_mla_mtp_decode.md", [_CSRC + "mla.hip"] + _COMMON),
     "mla_chunked_prefill": ("mla_decode_mla_chunked_prefill.md", [_CSRC + "mla.hip"] + _COMMON),
@@ -477,12 +478,13 @@ def main():
     bidx, pos = dev(case.new_batch_idx), dev(case.new_pos)
     slots = torch.empty(case.new_pos.size, dtype=torch.int32, device="cuda")
     out = torch.empty((case.q.shape[0], case.H, case.D), dtype=q.dtype, device="cuda")
+    out_code = pkv.PKV_BF16 if case.dtype == "bf16" else pkv.PKV_F32
     if case.kind == "decode":
         ws_bytes = pkv.paged_attn_decode_workspace(cache, case.B, case.H, case.max_blocks, case.scale,
-                                                   case.window, pkv.PKV_BF16 if case.dtype == "bf16" else pkv.PKV_F32,
-                                                   args.split_tokens)
+                                                   case.window, out_code, args.split_tokens)
     else:
-        ws_bytes = 0
+        ws_bytes = pkv.paged_attn_prefill_workspace(cache, case.B, case.H, case.max_blocks, case.q.shape[0],
+                                                    case.scale, case.window, out_code)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     max_q = int(np.diff(case.cu_seqlens_q).max(initial=0)) if case.kind == "prefill" else 1
     cu = dev(case.cu_seqlens_q)
@@ -521,7 +523,9 @@ def main():
     attn_gbs = a_b / (ms_attn * 1e-3) / 1e9
     attn_tflops = flops / (ms_attn * 1e-3) / 1e12
     kernel = "paged_attn_decode" if case.kind == "decode" else "paged_attn_prefill"
-    if case.kind == "prefill":
+    # The bound is the one the call's arithmetic intensity meets first: flops per
+    # algorithmic byte against the ridge of 2.5 PFLOP/s over 8 TB/s (312.5 flop/B).
+    if flops / a_b >= MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
     else:

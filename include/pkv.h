@@ -178,7 +178,13 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
                              const pkv_attn_params* params, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace paged_attn_prefill needs (0 is possible). */
+/* Bytes of workspace paged_attn_prefill needs (0 when the call is not split).
+ * Standard caches: when the (sequence, KV head, 128-column) workgroups of the call
+ * are too few to fill the GPU (multi-token decode: a few rows per sequence), the
+ * keys are split into partitions of at least 2048 and the fp32 partials
+ * ([total_q * H, partitions, head_dim] plus (m, l) pairs) are merged after the
+ * kernel.  The size depends on the arguments' sizes only (batch, heads, total_q,
+ * max_blocks_per_seq, block_size) and the GPU's CU count, never on device data. */
 size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache,
                                     int32_t total_q);
 
@@ -192,7 +198,8 @@ size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_pag
  *                  must already be in the cache (kv_cache_write first)
  *   max_q_len    : an upper bound of every n_b (sizes the grid)
  *   out          : [total_q, H, head_dim] in params->out_dtype
- * Standard caches need bf16 and head_dim 64 or 128.  MLA caches (absorbed form,
+ * Standard caches need bf16 and head_dim 64 or 128, and a workspace of the size
+ * paged_attn_prefill_workspace gives (PKV_ERR_WORKSPACE otherwise).  MLA caches (absorbed form,
  * the same constraints as decode) also cover multi-token decode (n_b of 2-4):
  * every query row is computed over all the keys it sees by one workgroup, so
  * no workspace is used and a row may span at most 1024 table blocks. */

@@ -269,6 +269,13 @@ def paged_attn_decode(q: torch.Tensor, cache: PagedKVCache, block_table: torch.T
     return out
 
 
+def paged_attn_prefill_workspace(cache: PagedKVCache, batch: int, num_q_heads: int, max_blocks_per_seq: int,
+                                 total_q: int, scale: float, window: int = 0, out_dtype: int = PKV_BF16) -> int:
+    """Bytes of workspace a prefill call of these sizes needs (0 when its keys are not split)."""
+    p = AttnParams(batch, num_q_heads, max_blocks_per_seq, scale, window, out_dtype, 0)
+    return int(load().paged_attn_prefill_workspace(ctypes.byref(p), ctypes.byref(cache.desc()), int(total_q)))
+
+
 def paged_attn_prefill(q: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,
                        cu_seqlens_q: torch.Tensor, seq_lens_kv: torch.Tensor, max_q_len: int,
                        scale: float, window: int = 0, q_rope: Optional[torch.Tensor] = None,

@@ -211,6 +211,45 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
   return plan;
 }
 
+// Prefill key split.  A prefill workgroup takes 128 query columns of one
+// (sequence, KV head) and walks every key they see; with few such workgroups
+// (multi-token decode: a handful of rows per sequence) the chip is not filled and
+// the longest sequence sets the time.  Then the keys are cut into partitions,
+// enough for about 8 workgroups per CU, of at least 2048 keys so that the fp32
+// partials stay a small fraction of the K/V bytes.  The plan uses only what the
+// workspace query also knows (rows per sequence from total_q, keys from the table
+// width), so both see the same partitions.
+struct PrefillPlan {
+  int32_t np = 1;
+  int32_t part_tiles = 0;
+  size_t ws_bytes = 0;
+  size_t ws_ml_offset = 0;
+};
+
+PrefillPlan plan_prefill(const pkv_attn_params* p, const pkv_paged_cache* c, int32_t total_q) {
+  PrefillPlan plan;
+  if (is_mla(c) || p->batch <= 0 || total_q <= 0) return plan;
+  const int64_t G = p->num_q_heads / c->num_kv_heads;
+  const int64_t rows_per_seq = ((int64_t)total_q + p->batch - 1) / p->batch;
+  const int64_t wgs = (int64_t)p->batch * c->num_kv_heads *
+                      ((rows_per_seq * G + pkv::kPrefillColumns - 1) / pkv::kPrefillColumns);
+  const int64_t cus = device_cu_count();
+  if (wgs >= 2 * cus) return plan;  // the grid fills the chip: one pass over the keys
+  const int64_t max_kv = (int64_t)p->max_blocks_per_seq * c->block_size;
+  const int64_t want = (8 * cus + wgs - 1) / wgs;  // partitions per workgroup
+  constexpr int64_t kMinPart = 2048;                // keys; a multiple of every block size and tile
+  const int64_t part = std::max<int64_t>(kMinPart, ((max_kv + want - 1) / want + kMinPart - 1) / kMinPart * kMinPart);
+  const int64_t np = (max_kv + part - 1) / part;
+  if (np <= 1) return plan;
+  plan.np = (int32_t)np;
+  plan.part_tiles = (int32_t)(part / pkv::kPrefillKeyTile);
+  const size_t rows = (size_t)total_q * p->num_q_heads * (size_t)np;
+  const size_t o_bytes = (rows * c->head_dim * sizeof(float) + 255) & ~size_t(255);
+  plan.ws_ml_offset = o_bytes;
+  plan.ws_bytes = o_bytes + rows * 2 * sizeof(float);
+  return plan;
+}
+
 }  // namespace
 
 extern "C" {
@@ -430,18 +469,14 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
 }
 
 size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache, int32_t total_q) {
-  (void)params;
-  (void)cache;
-  (void)total_q;
-  return 0;  // every prefill workgroup walks all keys of its rows: no partials
+  if (check_cache(cache) || check_params(params, cache) || total_q < 0) return 0;
+  return plan_prefill(params, cache, total_q).ws_bytes;
 }
 
 pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged_cache* cache,
                               const int32_t* block_table, const int32_t* cu_seqlens_q, const int32_t* seq_lens_kv,
                               int32_t total_q, int32_t max_q_len, const pkv_attn_params* params, void* out,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   pkv_status s = check_cache(cache);
   if (s) return s;
   s = check_params(params, cache);
@@ -494,7 +529,16 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
   if (!pkv::prefill_mfma_supported(cache->dtype, cache->head_dim))
     return fail(PKV_ERR_UNSUPPORTED, "prefill: needs bf16 and head_dim 64 or 128 (got dtype %d, head_dim %d)",
                 cache->dtype, cache->head_dim);
+  const PrefillPlan plan = plan_prefill(params, cache, total_q);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (plan.ws_bytes > 0 && !aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   pkv::PrefillArgs a{};
+  a.max_np = plan.np;
+  a.part_tiles = plan.part_tiles;
+  a.ws_o = plan.ws_bytes > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = plan.ws_bytes > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset) : nullptr;
   a.q = q;
   a.k_cache = cache->k_cache;
   a.v_cache = cache->v_cache;
@@ -512,7 +556,16 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
   a.window = params->window;
   a.scale_log2e = params->scale * pkv::kLog2e;
   a.out_dtype = params->out_dtype;
-  return from_hip(pkv::launch_prefill_mfma(a, static_cast<hipStream_t>(stream)), "prefill launch");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = pkv::launch_prefill_mfma(a, st);
+  if (e != hipSuccess) return from_hip(e, "prefill launch");
+  if (plan.np > 1) {
+    // rows = total_q query rows x H heads, every partition written
+    e = pkv::launch_decode_combine(a.ws_o, a.ws_ml, nullptr, total_q, params->num_q_heads, cache->head_dim,
+                                   plan.np, a.block_size_log2, 0, params->window, out, params->out_dtype, st);
+    if (e != hipSuccess) return from_hip(e, "prefill combine launch");
+  }
+  return ok();
 }
 
 }  // extern "C"

@@ -281,6 +281,8 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
 
 // One wave per (sequence, head): M = max_p m_p, L = sum_p l_p 2^(m_p - M),
 // out = (sum_p o_p 2^(m_p - M)) / L; a sequence with no key gets a zero row.
+// seq_lens == NULL (prefill rows): every one of the max_np partials was written
+// (an empty one as m = -inf, l = 0, o = 0) and all are merged.
 __global__ __launch_bounds__(kWave) void decode_combine_kernel(const float* __restrict__ ws_o,
                                                                const float* __restrict__ ws_ml,
                                                                const int32_t* __restrict__ seq_lens,
@@ -290,9 +292,8 @@ __global__ __launch_bounds__(kWave) void decode_combine_kernel(const float* __re
                                                                int32_t out_dtype) {
   extern __shared__ float s_w[];  // [max_np] weights 2^(m_p - M)
   const int64_t row = blockIdx.x;
-  const int b = (int)(row / H);
   const int lane = threadIdx.x;
-  const KeySpan sp = decode_span(seq_lens[b], window, bs_log2, bpp);
+  const KeySpan sp = seq_lens ? decode_span(seq_lens[row / H], window, bs_log2, bpp) : KeySpan{0, 0, 0, max_np};
   const float* ml = ws_ml + row * max_np * 2;
   float M = kNegInf;
   for (int p = lane; p < sp.np; p += kWave) M = fmaxf(M, ml[2 * p]);

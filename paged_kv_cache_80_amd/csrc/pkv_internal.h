@@ -114,7 +114,17 @@ struct PrefillArgs {
   float scale_log2e;
   int32_t out_dtype;
   int32_t q_tiles;  // query tiles per (sequence, KV head); set by the launcher
+  // Key split: with max_np > 1, workgroup partition y covers key tiles
+  // [y * part_tiles, (y + 1) * part_tiles) and leaves unnormalised partials
+  // ([total_q * H, max_np, head_dim] and (m, l) pairs) for the split-K combine.
+  int32_t max_np, part_tiles;
+  float* ws_o;
+  float* ws_ml;
 };
+// Query columns ((row, head) pairs of one KV head) per prefill workgroup, and keys
+// per tile; the host sizes the key split with them.
+constexpr int32_t kPrefillColumns = 128;
+constexpr int32_t kPrefillKeyTile = 64;
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t stream);
 // Widest block table the prefill kernel stages in LDS (256K tokens at 128-token blocks).
 constexpr int32_t kPrefillMaxTableBlocks = 2048;

@@ -41,6 +41,7 @@ constexpr int kColTiles = 2;                     // 16-column tiles per wave
 constexpr int kCols = kWaves * kColTiles * 16;   // columns per workgroup
 constexpr int kKeyTile = 64;                     // keys per LDS tile
 constexpr int kMaxTableLds = kPrefillMaxTableBlocks;  // block-table entries staged in LDS
+static_assert(kCols == kPrefillColumns && kKeyTile == kPrefillKeyTile, "host sizing");
 constexpr float kRescaleLog2 = 8.f;              // lazy-rescale threshold (log2 units)
 
 template <int D>
@@ -56,7 +57,12 @@ struct Tile {
   }
 };
 
-template <int D>
+// FEW: every workgroup holds fewer than kCols columns (a few query rows per
+// sequence, multi-token decode); then waves without a column skip the
+// arithmetic.  SPLIT: the keys are cut into partitions (blockIdx.y) that leave
+// partials.  Both are template flags so that the full-width, unsplit kernel
+// keeps their branches out of its schedule.
+template <int D, bool FEW, bool SPLIT>
 __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(PrefillArgs a) {
   using T = Tile<D>;
   constexpr int KS = D / 32;                       // 32-wide contraction steps of Q.K
@@ -122,9 +128,34 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   const int p_hi = L - n + last_col / G;
   const int key_lo = a.window > 0 ? max(0, p_lo - a.window + 1) : 0;
   const int key_hi = p_hi + 1;
-  if (key_hi <= key_lo) return;  // malformed lengths (n > L): nothing visible
-  const int t_begin = key_lo / kKeyTile;
-  const int t_end = (key_hi + kKeyTile - 1) / kKeyTile;
+  if constexpr (!SPLIT) {
+    if (key_hi <= key_lo) return;  // malformed lengths (n > L): nothing visible
+  }
+  int t_begin = key_lo / kKeyTile;
+  int t_end = (key_hi + kKeyTile - 1) / kKeyTile;
+  if constexpr (SPLIT) {
+    // This workgroup's key partition; with nothing visible in it (or malformed
+    // lengths) the workgroup leaves empty partials (m = -inf, l = 0, o = 0).
+    const int p0 = (int)blockIdx.y * a.part_tiles;
+    if (key_hi <= key_lo) t_end = t_begin;
+    t_begin = max(t_begin, p0);
+    t_end = max(t_begin, min(t_end, p0 + a.part_tiles));
+    if (t_begin >= t_end) {
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < kColTiles; ++ct) {
+        if (!cvalid[ct]) continue;
+        const int64_t pr = crow[ct] * a.max_np + blockIdx.y;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) store4(a.ws_o, pr * D + 16 * dt + 4 * lg, z, PKV_F32);
+        if (lg == 0) {
+          a.ws_ml[2 * pr] = kNegInf;
+          a.ws_ml[2 * pr + 1] = 0.f;
+        }
+      }
+      return;
+    }
+  }
 
   const int bs_log2 = a.block_size_log2;
   const int bs_mask = (1 << bs_log2) - 1;
@@ -307,20 +338,51 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  issue_tile(B0{}, t_begin);
+  // A wave whose columns all lie past the last one copies its share of every
+  // tile but skips the arithmetic.
+  const bool wave_cols = col0 + wave * kColTiles * 16 < ncols;
+  issue_tile(B0{}, t_begin);  // t_begin < t_end here
   for (int tile = t_begin; tile < t_end; tile += 2) {
     wait_vmem();
     __syncthreads();  // buffer 0 holds `tile`; nobody reads buffer 1 any more
     if (tile + 1 < t_end) issue_tile(B1{}, tile + 1);
-    compute_tile(B0{}, tile);
+    if constexpr (FEW) {
+      if (wave_cols) compute_tile(B0{}, tile);
+    } else {
+      compute_tile(B0{}, tile);
+    }
     if (tile + 1 < t_end) {
       wait_vmem();
       __syncthreads();  // buffer 1 holds tile+1; nobody reads buffer 0 any more
       if (tile + 2 < t_end) issue_tile(B0{}, tile + 2);
-      compute_tile(B1{}, tile + 1);
+      if constexpr (FEW) {
+        if (wave_cols) compute_tile(B1{}, tile + 1);
+      } else {
+        compute_tile(B1{}, tile + 1);
+      }
     }
   }
 
+  if (SPLIT) {
+    // Partials of this key partition: unnormalised o, the reference maximum
+    // (log2 units) and the sum; a column that saw no key here leaves (-inf, 0, 0).
+#pragma unroll
+    for (int ct = 0; ct < kColTiles; ++ct) {
+      const float ls = row4_sum(l[ct]);
+      if (!cvalid[ct]) continue;
+      const int64_t pr = crow[ct] * a.max_np + blockIdx.y;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float v[4] = {o[ct][dt][0], o[ct][dt][1], o[ct][dt][2], o[ct][dt][3]};
+        store4(a.ws_o, pr * D + 16 * dt + 4 * lg, v, PKV_F32);
+      }
+      if (lg == 0) {
+        a.ws_ml[2 * pr] = mref[ct];
+        a.ws_ml[2 * pr + 1] = ls;
+      }
+    }
+    return;
+  }
   // Normalise and store: lane holds column l16, dimensions 16*dt + 4*lg + r.
 #pragma unroll
   for (int ct = 0; ct < kColTiles; ++ct) {
@@ -333,6 +395,16 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
       store4(a.out, crow[ct] * D + 16 * dt + 4 * lg, v, a.out_dtype);
     }
   }
+}
+
+template <int D>
+void launch_variant(const PrefillArgs& a, dim3 grid, bool few, bool split, hipStream_t stream) {
+  // A split call always takes the few-column variant: its per-wave column test
+  // is exact for any width, and that variant fits its registers.
+  const dim3 blk(kWaves * kWave);
+  if (split) prefill_mfma_kernel<D, true, true><<<grid, blk, 0, stream>>>(a);
+  else if (few) prefill_mfma_kernel<D, true, false><<<grid, blk, 0, stream>>>(a);
+  else prefill_mfma_kernel<D, false, false><<<grid, blk, 0, stream>>>(a);
 }
 
 }  // namespace
@@ -349,11 +421,14 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a_in, hipStream_t stream) {
   if (tiles == 0 || a.batch == 0) return hipSuccess;
   const int64_t total = tiles * a.num_kv_heads * a.batch;
   const int64_t padded = (total + 7) / 8 * 8;
-  if (padded > 0x7fffffff) return hipErrorInvalidValue;
+  if (padded > 0x7fffffff || a.max_np < 1 || a.max_np > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)padded, (unsigned)a.max_np);
+  const bool few = cols < kCols;
+  const bool split = a.max_np > 1;
   a.q_tiles = (int32_t)tiles;
   switch (a.head_dim) {
-    case 64: prefill_mfma_kernel<64><<<(unsigned)padded, kWaves * kWave, 0, stream>>>(a); break;
-    case 128: prefill_mfma_kernel<128><<<(unsigned)padded, kWaves * kWave, 0, stream>>>(a); break;
+    case 64: launch_variant<64>(a, grid, few, split, stream); break;
+    case 128: launch_variant<128>(a, grid, few, split, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -131,6 +131,23 @@ def test_stream_workspace_layout(lib):
     assert 0 <= sizes[1] - sizes[0] - 4 * piece < 256 + 4
 
 
+def test_prefill_workspace_of_the_key_split(lib):
+    """A multi-token decode (4 rows per sequence, G = 2: one 128-column workgroup per
+    sequence and KV head, 8 in all) over up to 8192 keys is split into 4 partitions of 2048
+    keys: partials for total_q x H rows x 4 (head_dim floats, 256-byte aligned, then (m, l)
+    pairs).  A grid that fills the GPU (the chunked prefill shapes) takes no workspace."""
+    c = _cache()  # bf16, H_kv = 4, head_dim 128, block_size 128
+    p = _params(batch=2, num_q_heads=8, max_blocks_per_seq=64)
+    rows = 8 * 8 * 4
+    need = lib.paged_attn_prefill_workspace(ctypes.byref(p), ctypes.byref(c), 8)
+    assert need == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
+    rc = lib.paged_attn_prefill(FAKE, None, ctypes.byref(c), FAKE, FAKE, FAKE, 8, 4, ctypes.byref(p), FAKE,
+                                None, 0, None)
+    assert rc == 3 and "workspace" in lib.pkv_last_error().decode()
+    big = _params(batch=8, num_q_heads=32, max_blocks_per_seq=36)
+    assert lib.paged_attn_prefill_workspace(ctypes.byref(big), ctypes.byref(_cache(num_kv_heads=8)), 4096) == 0
+
+
 def test_write_rejects_malformed_arguments(lib):
     c = _cache()
     assert lib.kv_cache_write(FAKE, 4, FAKE, None, None, ctypes.byref(c), None) == 1  # v missing

@@ -313,6 +313,12 @@ def test_gqa_decode_70b_full_size(orc, window):
     _full_size_check(orc, workloads.gqa_decode_70b(0, window=window))
 
 
+def test_gqa_mtp_decode_full_size(orc):
+    """Multi-token decode on the 70B shapes: 4 causal query rows per sequence, ragged
+    1K-32K, null block 0 (NaN-filled); the prefill kernel at its bench launch (sampled rows)."""
+    _full_size_check(orc, workloads.gqa_mtp_decode(0))
+
+
 # --------------------------------------------------------------------------- tables from the allocator
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

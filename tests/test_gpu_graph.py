@@ -52,7 +52,8 @@ def test_step_replays_in_a_graph(name):
         ws_bytes = pkv.paged_attn_decode_workspace(d.cache, case.B, case.H, case.max_blocks, case.scale, case.window,
                                                    pkv.PKV_BF16 if ref.dtype == torch.bfloat16 else pkv.PKV_F32)
     else:
-        ws_bytes = 0
+        ws_bytes = pkv.paged_attn_prefill_workspace(d.cache, case.B, case.H, case.max_blocks, case.q.shape[0],
+                                                    case.scale, case.window, pkv.PKV_BF16)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     max_q = int(np.diff(case.cu_seqlens_q).max(initial=0)) if case.kind == "prefill" else 1
 

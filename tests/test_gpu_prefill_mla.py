@@ -58,6 +58,35 @@ def test_prefill_matches_oracle(orc, shape):
     assert_rows_close(out, ref, BF16_TOL)
 
 
+# Multi-token decode shapes: so few (sequence, KV head, column tile) workgroups that the
+# keys are split into partitions of 2048 and the partials merged by the combine --
+# partitions past a short sequence or before its window are empty.
+SPLIT_MATRIX = [
+    # B, H, Hkv, D, bs, cached, new, window
+    (3, 16, 4, 128, 128, [5000, 100, 9000], [4, 2, 3], 0),
+    (2, 8, 2, 64, 32, [6000, 3000], [4, 1], 1000),
+    (4, 32, 8, 128, 64, [2047, 2048, 4095, 4100], [1, 2, 3, 4], 0),  # rows on partition edges
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_MATRIX)
+def test_prefill_key_split_matches_oracle(orc, shape):
+    import paged_kv_cache_80_amd as pkv
+
+    B, H, Hkv, D, bs, cached, new, w = shape
+    case = workloads.prefill_case(sum(cached) + w + 1, B, H, Hkv, D, "bf16", cached=cached, new=new,
+                                  block_size=bs, window=w, null_block=True)
+    d = DeviceCase(case)
+    need = pkv.paged_attn_prefill_workspace(d.cache, B, H, case.max_blocks, case.q.shape[0], case.scale, w)
+    assert need > 0, "these shapes take the key split"
+    ref, c_ref, slots_ref = oracle_run(orc, case)
+    out, slots = d.run()
+    np.testing.assert_array_equal(host(slots), slots_ref)
+    assert_rows_close(out, ref, BF16_TOL)
+    out32 = d.attend(out_dtype=torch.float32)
+    assert_rows_close(out32, ref, ACC_TOL)
+
+
 def test_prefill_fp32_accumulation(orc):
     case = workloads.prefill_case(7, 3, 16, 4, 128, "bf16", cached=[700, 0, 260], new=[100, 300, 64],
                                   block_size=64, null_block=True)

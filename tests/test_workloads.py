@@ -52,5 +52,8 @@ def test_full_size_workload_shapes():
     assert sorted(c.block_table.ravel().tolist()) == list(range(1024))  # a permutation of the whole pool
     p = workloads.chunked_prefill(0)
     assert p.q.shape == (4096, 32, 128) and p.cu_seqlens_q.tolist() == list(range(0, 4097, 512))
+    t = workloads.gqa_mtp_decode(0)
+    assert t.q.shape == (128, 64, 128) and np.all(np.diff(t.cu_seqlens_q) == 4)
+    assert t.seq_lens.min() >= 1024 and t.seq_lens.max() <= 32768 and t.null_block
     m = workloads.mla_latent_write(0)
     assert m.latent.shape == (32768, 576) and m.cache_nope.shape[1:] == (128, 1, 512)

@@ -397,6 +397,16 @@ def chunked_prefill(seed: int = 0) -> Case:
                         name="chunked_prefill")
 
 
+def gqa_mtp_decode(seed: int = 0) -> Case:
+    """Multi-token decode on the llama2-70B layer shapes: B=32, H=64, H_kv=8, d_h=128,
+    total lengths uniform in [1024, 32768] (drawn from their own seeded stream), of which
+    the last 4 positions of every sequence are new query rows under the bottom-right
+    causal mask; shuffled table over a pool with 10% spare blocks and null block 0."""
+    L = np.random.default_rng([seed, 70]).integers(1024, 32769, size=32).astype(np.int32)
+    return prefill_case(seed, 32, 64, 8, 128, "bf16", cached=L - 4, new=4, max_blocks=256, null_block=True,
+                        name="gqa_mtp_decode")
+
+
 def mla_decode(seed: int = 0) -> Case:
     """MLA absorbed decode: B=64, 128 query heads, latent 512 + rope 64, every
     length 8192, table = a permutation of 4096 blocks, scale 1/sqrt(576)."""
@@ -436,6 +446,7 @@ WORKLOADS = {
     "mha_decode_7b_int8": lambda seed=0: mha_decode_7b(seed, int8=True),
     "gqa_decode_70b_int8": lambda seed=0: gqa_decode_70b(seed, int8=True),
     "chunked_prefill": chunked_prefill,
+    "gqa_mtp_decode": gqa_mtp_decode,
     "mla_decode": mla_decode,
     "mla_mtp_decode": mla_mtp_decode,
     "mla_chunked_prefill": mla_chunked_prefill,
