@@ -215,8 +215,10 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
 // (sequence, KV head) and walks every key they see; with few such workgroups
 // (multi-token decode: a handful of rows per sequence) the chip is not filled and
 // the longest sequence sets the time.  Then the keys are cut into partitions,
-// enough for about 8 workgroups per CU, of at least 2048 keys so that the fp32
-// partials stay a small fraction of the K/V bytes.  The plan uses only what the
+// enough for about 16 workgroups per CU (ragged lengths leave many partitions
+// empty), of at least 2048 keys so that the fp32 partials stay a small fraction
+// of the K/V bytes (8, 32 and 64 per CU, and 1024- or 512-key partitions, measured
+// slower on the 70B multi-token decode).  The plan uses only what the
 // workspace query also knows (rows per sequence from total_q, keys from the table
 // width), so both see the same partitions.
 struct PrefillPlan {
@@ -236,7 +238,7 @@ PrefillPlan plan_prefill(const pkv_attn_params* p, const pkv_paged_cache* c, int
   const int64_t cus = device_cu_count();
   if (wgs >= 2 * cus) return plan;  // the grid fills the chip: one pass over the keys
   const int64_t max_kv = (int64_t)p->max_blocks_per_seq * c->block_size;
-  const int64_t want = (8 * cus + wgs - 1) / wgs;  // partitions per workgroup
+  const int64_t want = (16 * cus + wgs - 1) / wgs;  // partitions per workgroup
   constexpr int64_t kMinPart = 2048;                // keys; a multiple of every block size and tile
   const int64_t part = std::max<int64_t>(kMinPart, ((max_kv + want - 1) / want + kMinPart - 1) / kMinPart * kMinPart);
   const int64_t np = (max_kv + part - 1) / part;
