@@ -57,14 +57,19 @@ struct Tile {
   }
 };
 
-// FEW: every workgroup holds fewer than kCols columns (a few query rows per
-// sequence, multi-token decode); then waves without a column skip the
-// arithmetic.  SPLIT: the keys are cut into partitions (blockIdx.y) that leave
+// FEW (the narrow variant: split calls, and calls whose columns fit in one
+// full-width workgroup, as a few query rows per sequence do): one 16-column tile
+// per wave, so a call's columns spread over twice as many waves, and waves
+// without a column skip the arithmetic.  SPLIT: the keys are cut into partitions (blockIdx.y) that leave
 // partials.  Both are template flags so that the full-width, unsplit kernel
 // keeps their branches out of its schedule.
 template <int D, bool FEW, bool SPLIT>
 __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(PrefillArgs a) {
   using T = Tile<D>;
+  // 16-column tiles per wave: two, or one when the workgroup's columns are few
+  // (then the columns of a call spread over twice as many waves).
+  constexpr int CT = FEW ? 1 : kColTiles;
+  constexpr int COLS = kWaves * CT * 16;  // columns per workgroup
   constexpr int KS = D / 32;                       // 32-wide contraction steps of Q.K
   constexpr int DT = D / 16;                       // 16-row tiles of O^T
   constexpr int NU = kKeyTile / 16;
@@ -99,18 +104,18 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   const int n = a.cu_seqlens_q[b + 1] - q0;
   const int L = a.seq_lens_kv[b];
   const int ncols = n * G;
-  const int col0 = qt * kCols;
+  const int col0 = qt * COLS;
   if (col0 >= ncols) return;
 
   // This lane's columns and their q fragments.
-  bool cvalid[kColTiles];
-  int cpos[kColTiles];
-  int64_t crow[kColTiles];
-  uint4 qf[kColTiles][KS];
+  bool cvalid[CT];
+  int cpos[CT];
+  int64_t crow[CT];
+  uint4 qf[CT][KS];
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
 #pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct) {
-    const int gc = col0 + (wave * kColTiles + ct) * 16 + l16;
+  for (int ct = 0; ct < CT; ++ct) {
+    const int gc = col0 + (wave * CT + ct) * 16 + l16;
     cvalid[ct] = gc < ncols;
     const int i = cvalid[ct] ? gc / G : 0;
     const int hl = cvalid[ct] ? gc - i * G : 0;
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
 
   retire_loads();  // q fragments are in registers before any tile is in flight
   // Keys any column of this workgroup can see.
-  const int last_col = min(ncols - 1, col0 + kCols - 1);
+  const int last_col = min(ncols - 1, col0 + COLS - 1);
   const int p_lo = L - n + col0 / G;
   const int p_hi = L - n + last_col / G;
   const int key_lo = a.window > 0 ? max(0, p_lo - a.window + 1) : 0;
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
     if (t_begin >= t_end) {
       const float z[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ct = 0; ct < kColTiles; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         if (!cvalid[ct]) continue;
         const int64_t pr = crow[ct] * a.max_np + blockIdx.y;
 #pragma unroll
@@ -210,10 +215,10 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
     }
   };
 
-  f32x4_t o[kColTiles][DT];
-  float mref[kColTiles], l[kColTiles];  // mref: reference maximum in log2 units
+  f32x4_t o[CT][DT];
+  float mref[CT], l[CT];  // mref: reference maximum in log2 units
 #pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct) {
+  for (int ct = 0; ct < CT; ++ct) {
     mref[ct] = kNegInf;
     l[ct] = 0.f;
 #pragma unroll
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
     const int j0 = tile * kKeyTile;
 
     // S^T = K . Q^T
-    f32x4_t s[kColTiles][NU];
+    f32x4_t s[CT][NU];
     uint4 kf[2][KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[0][ks] = *reinterpret_cast<const uint4*>(kb + T::off(0, 64 * ks));
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
           s[ct][u] = mfma_bf16(kf[u & 1][ks], qf[ct][ks], ks == 0 ? f32x4_zero() : s[ct][u]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -270,9 +275,9 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
     // probabilities up to 256 accumulate against the stale reference, which is
     // exact (O and l share it) and skips the O rescale on almost every tile.
     const bool full = j0 >= key_lo && j0 + kKeyTile - 1 <= p_lo && (a.window == 0 || j0 > p_hi - a.window);
-    uint4 phi[kColTiles][kKeyTile / 32], plo[kColTiles][kKeyTile / 32];
+    uint4 phi[CT][kKeyTile / 32], plo[CT][kKeyTile / 32];
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       if (!full) {
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) {
+        for (int ct = 0; ct < CT; ++ct) {
           o[ct][dt] = mfma_bf16(vf[kk & 1][dt], phi[ct][kk], o[ct][dt]);
           o[ct][dt] = mfma_bf16(vf[kk & 1][dt], plo[ct][kk], o[ct][dt]);
         }
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   using B1 = std::integral_constant<int, 1>;
   // A wave whose columns all lie past the last one copies its share of every
   // tile but skips the arithmetic.
-  const bool wave_cols = col0 + wave * kColTiles * 16 < ncols;
+  const bool wave_cols = col0 + wave * CT * 16 < ncols;
   issue_tile(B0{}, t_begin);  // t_begin < t_end here
   for (int tile = t_begin; tile < t_end; tile += 2) {
     wait_vmem();
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
     // Partials of this key partition: unnormalised o, the reference maximum
     // (log2 units) and the sum; a column that saw no key here leaves (-inf, 0, 0).
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       const float ls = row4_sum(l[ct]);
       if (!cvalid[ct]) continue;
       const int64_t pr = crow[ct] * a.max_np + blockIdx.y;
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
   }
   // Normalise and store: lane holds column l16, dimensions 16*dt + 4*lg + r.
 #pragma unroll
-  for (int ct = 0; ct < kColTiles; ++ct) {
+  for (int ct = 0; ct < CT; ++ct) {
     const float ls = row4_sum(l[ct]);
     if (!cvalid[ct]) continue;
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
@@ -398,12 +403,12 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
 }
 
 template <int D>
-void launch_variant(const PrefillArgs& a, dim3 grid, bool few, bool split, hipStream_t stream) {
-  // A split call always takes the few-column variant: its per-wave column test
-  // is exact for any width, and that variant fits its registers.
+void launch_variant(const PrefillArgs& a, dim3 grid, bool narrow, bool split, hipStream_t stream) {
+  // A split call always takes the narrow variant (the wide split one does not fit
+  // its registers); the grid's column tiles were sized for it.
   const dim3 blk(kWaves * kWave);
   if (split) prefill_mfma_kernel<D, true, true><<<grid, blk, 0, stream>>>(a);
-  else if (few) prefill_mfma_kernel<D, true, false><<<grid, blk, 0, stream>>>(a);
+  else if (narrow) prefill_mfma_kernel<D, true, false><<<grid, blk, 0, stream>>>(a);
   else prefill_mfma_kernel<D, false, false><<<grid, blk, 0, stream>>>(a);
 }
 
@@ -417,18 +422,22 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a_in, hipStream_t stream) {
   PrefillArgs a = a_in;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t cols = (int64_t)a.max_q_len * G;
-  const int64_t tiles = (cols + kCols - 1) / kCols;
+  // Split calls, and calls whose columns fit in one full-width workgroup, take the
+  // narrow variant (FEW: one 16-column tile per wave, waves without a column skip
+  // the arithmetic); its workgroups hold half as many columns.
+  const bool split = a.max_np > 1;
+  const bool narrow = split || cols < kCols;
+  const int64_t width = narrow ? kCols / 2 : kCols;
+  const int64_t tiles = (cols + width - 1) / width;
   if (tiles == 0 || a.batch == 0) return hipSuccess;
   const int64_t total = tiles * a.num_kv_heads * a.batch;
   const int64_t padded = (total + 7) / 8 * 8;
   if (padded > 0x7fffffff || a.max_np < 1 || a.max_np > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)padded, (unsigned)a.max_np);
-  const bool few = cols < kCols;
-  const bool split = a.max_np > 1;
   a.q_tiles = (int32_t)tiles;
   switch (a.head_dim) {
-    case 64: launch_variant<64>(a, grid, few, split, stream); break;
-    case 128: launch_variant<128>(a, grid, few, split, stream); break;
+    case 64: launch_variant<64>(a, grid, narrow, split, stream); break;
+    case 128: launch_variant<128>(a, grid, narrow, split, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
