@@ -66,6 +66,8 @@ SPLIT_MATRIX = [
     (3, 16, 4, 128, 128, [5000, 100, 9000], [4, 2, 3], 0),
     (2, 8, 2, 64, 32, [6000, 3000], [4, 1], 1000),
     (4, 32, 8, 128, 64, [2047, 2048, 4095, 4100], [1, 2, 3, 4], 0),  # rows on partition edges
+    (1, 16, 2, 128, 128, [20000], [40], 0),     # 320 columns: several column tiles per partition
+    (1, 16, 2, 64, 64, [9000], [100], 3000),    # 800 columns under a window
 ]
 
 
