@@ -114,6 +114,13 @@ pkv_status pkv_resolve_slots(const int32_t* block_table, int32_t batch, int32_t 
                              int32_t block_size, const int32_t* batch_idx, const int32_t* pos,
                              int32_t n, int32_t* slots_out, void* stream);
 
+/* The same resolution without the batch count (the row stride alone addresses
+ * block_table): slots_out[i] for i < n exactly as pkv_resolve_slots computes it.
+ * Same errors, except that there is no batch to check. */
+pkv_status paged_resolve_slots(const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size,
+                               const int32_t* batch_idx, const int32_t* pos, int32_t n, int32_t* slots_out,
+                               void* stream);
+
 /* Cache write ("Ascend NPU standalone-deployment KVCache guide", mode 2: the
  * scatter into the cache viewed as [num_blocks*block_size, num_kv_heads, head_dim]).
  * Row t of k (and v, and k_rope) is copied bit for bit to cache row slot_mapping[t];

@@ -28,7 +28,7 @@ STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED", 3: "P
           4: "PKV_ERR_HIP"}
 
 # Every symbol include/pkv.h declares.
-EXPORTS = ("pkv_resolve_slots", "kv_cache_write", "kv_rmsnorm_rope_cache", "paged_attn_decode_workspace",
+EXPORTS = ("pkv_resolve_slots", "paged_resolve_slots", "kv_cache_write", "kv_rmsnorm_rope_cache", "paged_attn_decode_workspace",
            "paged_attn_decode", "paged_attn_prefill_workspace", "paged_attn_prefill", "pkv_last_error",
            "pkv_version")
 
@@ -69,6 +69,7 @@ def load(path: str = LIB_PATH):
     P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pc, pp = ctypes.POINTER(PagedCacheDesc), ctypes.POINTER(AttnParams)
     lib.pkv_resolve_slots.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
+    lib.paged_resolve_slots.argtypes = [P, i32, i32, P, P, i32, P, P]
     lib.kv_cache_write.argtypes = [P, i32, P, P, P, pc, P]
     lib.kv_rmsnorm_rope_cache.argtypes = [P, P, P, P, P, i32, ctypes.c_float, i32, pc, P, P, P]
     lib.paged_attn_decode_workspace.argtypes = [pp, pc]
@@ -77,7 +78,7 @@ def load(path: str = LIB_PATH):
     lib.paged_attn_prefill_workspace.argtypes = [pp, pc, i32]
     lib.paged_attn_prefill_workspace.restype = sz
     lib.paged_attn_prefill.argtypes = [P, P, pc, P, P, P, i32, i32, pp, P, P, sz, P]
-    for f in (lib.pkv_resolve_slots, lib.kv_cache_write, lib.kv_rmsnorm_rope_cache, lib.paged_attn_decode,
+    for f in (lib.pkv_resolve_slots, lib.paged_resolve_slots, lib.kv_cache_write, lib.kv_rmsnorm_rope_cache, lib.paged_attn_decode,
               lib.paged_attn_prefill):
         f.restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -180,6 +181,23 @@ def pkv_resolve_slots(block_table: torch.Tensor, block_size: int, batch_idx: tor
     _check(load().pkv_resolve_slots(_ptr(bt), bt.shape[0], bt.shape[1], block_size,
                                     _ptr(_i32(batch_idx)), _ptr(_i32(pos)), n, _ptr(slots_out),
                                     _stream(stream)))
+    return slots_out
+
+
+def paged_resolve_slots(block_table: torch.Tensor, block_size: int, batch_idx: torch.Tensor,
+                        pos: torch.Tensor, slots_out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """pkv_resolve_slots through the entry point that takes no batch count."""
+    bt = _i32(block_table)
+    n = batch_idx.numel()
+    if bt.dim() != 2:
+        raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+    _expect(pos, (n,), "pos")
+    _expect(slots_out, (n,), "slots_out")
+    if slots_out is None:
+        slots_out = torch.empty(n, dtype=torch.int32, device=bt.device)
+    _check(load().paged_resolve_slots(_ptr(bt), bt.shape[1], block_size, _ptr(_i32(batch_idx)),
+                                      _ptr(_i32(pos)), n, _ptr(slots_out), _stream(stream)))
     return slots_out
 
 

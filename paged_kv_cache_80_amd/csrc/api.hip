@@ -273,6 +273,19 @@ pkv_status pkv_resolve_slots(const int32_t* block_table, int32_t batch, int32_t 
                   "pkv_resolve_slots launch");
 }
 
+pkv_status paged_resolve_slots(const int32_t* block_table, int32_t max_blocks_per_seq, int32_t block_size,
+                               const int32_t* batch_idx, const int32_t* pos, int32_t n, int32_t* slots_out,
+                               void* stream) {
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n %d must be >= 0", n);
+  if (n == 0) return ok();
+  if (!block_table || !batch_idx || !pos || !slots_out) return fail(PKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0");
+  if (!pow2_block(block_size)) return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not one of 16, 32, 64, 128", block_size);
+  return from_hip(pkv::launch_resolve_slots(block_table, 0, max_blocks_per_seq, block_size, batch_idx, pos, n,
+                                            slots_out, static_cast<hipStream_t>(stream)),
+                  "paged_resolve_slots launch");
+}
+
 pkv_status kv_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const void* k, const void* v,
                           const void* k_rope, const pkv_paged_cache* cache, void* stream) {
   pkv_status s = check_cache(cache);

@@ -162,6 +162,10 @@ def test_resolve_rejects_malformed_arguments(lib):
     assert lib.pkv_resolve_slots(FAKE, 2, 4, 100, FAKE, FAKE, 3, FAKE, None) == 2
     assert lib.pkv_resolve_slots(None, 2, 4, 128, FAKE, FAKE, 3, FAKE, None) == 1
     assert lib.pkv_resolve_slots(FAKE, 2, 4, 128, FAKE, FAKE, 0, FAKE, None) == 0
+    assert lib.paged_resolve_slots(FAKE, 4, 100, FAKE, FAKE, 3, FAKE, None) == 2
+    assert lib.paged_resolve_slots(None, 4, 128, FAKE, FAKE, 3, FAKE, None) == 1
+    assert lib.paged_resolve_slots(FAKE, 0, 128, FAKE, FAKE, 3, FAKE, None) == 1
+    assert lib.paged_resolve_slots(FAKE, 4, 128, FAKE, FAKE, 0, FAKE, None) == 0
 
 
 def test_empty_batch_is_a_no_op(lib):

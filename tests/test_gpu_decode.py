@@ -88,6 +88,8 @@ def test_resolve_matches_oracle(orc, bs):
     ok = pos >= 0
     want = np.full(n, -1, np.int32)
     want[ok] = orc.resolve_slots(bt, bs, nb, bidx[ok], pos[ok])
+    # the entry point without the batch count gives the same slots
+    np.testing.assert_array_equal(host(pkv.paged_resolve_slots(dev(bt), bs, dev(bidx), dev(pos))), got)
     np.testing.assert_array_equal(got, want)
 
 
