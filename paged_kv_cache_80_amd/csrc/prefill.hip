@@ -57,18 +57,17 @@ struct Tile {
   }
 };
 
-// FEW (the narrow variant: split calls, and calls whose columns fit in one
+// FEW, the narrow variant (split calls, and calls whose columns fit in one
 // full-width workgroup, as a few query rows per sequence do): one 16-column tile
-// per wave, so a call's columns spread over twice as many waves, and waves
-// without a column skip the arithmetic.  SPLIT: the keys are cut into partitions (blockIdx.y) that leave
-// partials.  Both are template flags so that the full-width, unsplit kernel
-// keeps their branches out of its schedule.
+// per wave instead of two, so a call's columns spread over twice as many waves,
+// and waves without a column skip the arithmetic.  SPLIT: the keys are cut into
+// partitions (blockIdx.y) that leave partials for the combine.  Both are
+// template flags so that the full-width, unsplit kernel keeps their branches out
+// of its schedule.
 template <int D, bool FEW, bool SPLIT>
 __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(PrefillArgs a) {
   using T = Tile<D>;
-  // 16-column tiles per wave: two, or one when the workgroup's columns are few
-  // (then the columns of a call spread over twice as many waves).
-  constexpr int CT = FEW ? 1 : kColTiles;
+  constexpr int CT = FEW ? 1 : kColTiles;  // 16-column tiles per wave
   constexpr int COLS = kWaves * CT * 16;  // columns per workgroup
   constexpr int KS = D / 32;                       // 32-wide contraction steps of Q.K
   constexpr int DT = D / 16;                       // 16-row tiles of O^T
