@@ -11,7 +11,7 @@
 // Work split.  One workgroup per (sequence, key partition, group of up to 128
 // heads); each wave owns 16 heads and keeps their q (576 bf16) in registers and
 // their O^T (512 x 16 fp32) in accumulators.  32-key tiles of the latent are
-// copied straight into LDS with global_load_lds, double-buffered, one row per
+// copied straight into LDS with global_load_lds through a ring of slots, one row per
 // wave instruction (rows padded so fragment reads spread over the banks); the
 // rope rows sit in a second, chunk-swizzled tile.  The same row-major latent
 // tile feeds S^T = C.Q^T (ds_read_b128) and, through ds_read_b64_tr_b16, the
@@ -57,7 +57,7 @@ __device__ __forceinline__ void wait_tile(int ahead) {
   wait_vm<0>();
 }
 
-// NW waves of 16 heads; NBUF key tiles in an LDS ring (NBUF - 1 in flight);
+// NW waves of 16 heads; NBUF key tiles in an LDS ring (kLead of them in flight);
 // QD / PD fragment reads in flight ahead of the Q.K / P.V MFMAs.
 template <int NW, int NBUF, int QD, int PD>
 __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs a) {
@@ -70,6 +70,11 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
   constexpr int NL_LO = kRows + (kRopeLoads + NW - 1) / NW;  // waves < kRopeLoads % NW (or all)
   constexpr int NL_HI = kRows + kRopeLoads / NW;
   static_assert(kKeyTile % NW == 0 && NBUF >= 2 && NBUF <= 4, "tile split");
+  // Tiles in flight beyond the current one.  The 4-slot ring keeps two, so a slot
+  // is refilled two barriers after its last read; against three in flight it
+  // measured 0-2 % faster on MLA decode and equal on the multi-token decode and
+  // the chunked prefill.
+  constexpr int kLead = NBUF >= 4 ? NBUF - 2 : NBUF - 1;
   __shared__ __attribute__((aligned(16))) uint16_t c_lds[NBUF][kKeyTile][kRow];
   __shared__ __attribute__((aligned(16))) uint16_t r_lds[NBUF][kKeyTile][kR];
   __shared__ int32_t s_blk[kMaxBpp];
@@ -197,19 +202,19 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
   const int t_first = tok_begin & ~(kKeyTile - 1);
   const int ntiles = (tok_end - t_first + kKeyTile - 1) / kKeyTile;
 #pragma unroll
-  for (int k = 0; k < NBUF - 1; ++k)
+  for (int k = 0; k < kLead; ++k)
     if (k < ntiles) issue_tile(t_first + k * kKeyTile, k);
 
   for (int it = 0; it < ntiles; ++it) {
     const int t0 = t_first + it * kKeyTile;
     const int buf = it % NBUF;
-    const int ahead = min(NBUF - 2, ntiles - 1 - it);
+    const int ahead = min(kLead - 1, ntiles - 1 - it);
     if (wave < kRopeLoads % NW || kRopeLoads % NW == 0)
-      wait_tile<NL_LO, NBUF - 2>(ahead);
+      wait_tile<NL_LO, kLead - 1>(ahead);
     else
-      wait_tile<NL_HI, NBUF - 2>(ahead);
-    __syncthreads();  // tile it is visible; slot (it - 1) % NBUF is free
-    if (it + NBUF - 1 < ntiles) issue_tile(t0 + (NBUF - 1) * kKeyTile, (it + NBUF - 1) % NBUF);
+      wait_tile<NL_HI, kLead - 1>(ahead);
+    __syncthreads();  // tile it is visible; slot (it + kLead) % NBUF was last read before it
+    if (it + kLead < ntiles) issue_tile(t0 + kLead * kKeyTile, (it + kLead) % NBUF);
 
     // S^T = C.Q^T over 18 contraction steps for both 16-key halves, the steps
     // of the two halves interleaved; each fragment is read QD steps ahead of
