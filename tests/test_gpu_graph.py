@@ -34,6 +34,8 @@ CASES = {
                                                 len_range=(1, 1200), rope_dim=64, scale=576 ** -0.5),
     "chunked prefill": lambda: workloads.prefill_case(9, 3, 16, 4, 128, "bf16", cached=[100, 0, 700],
                                                       new=[60, 33, 128], block_size=64),
+    "multi-token decode (key split + combine)": lambda: workloads.prefill_case(
+        10, 3, 16, 4, 128, "bf16", cached=[5000, 100, 3000], new=[4, 2, 3], block_size=128, null_block=True),
 }
 
 
@@ -55,6 +57,8 @@ def test_step_replays_in_a_graph(name):
         ws_bytes = pkv.paged_attn_prefill_workspace(d.cache, case.B, case.H, case.max_blocks, case.q.shape[0],
                                                     case.scale, case.window, pkv.PKV_BF16)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    if "split" in name:
+        assert ws_bytes > 0, "this case takes the key split"
     max_q = int(np.diff(case.cu_seqlens_q).max(initial=0)) if case.kind == "prefill" else 1
 
     def step():
