@@ -26,7 +26,11 @@
  *     status, launches nothing and leaves a message for pkv_last_error().
  *     The CONTENTS of device index arrays are trusted: a block id outside
  *     [0, num_blocks), a sequence length beyond max_blocks_per_seq *
- *     block_size or a slot outside the cache is undefined behaviour.
+ *     block_size or a slot outside the cache is undefined behaviour.  The
+ *     Python binding can check them on the host before each launch (its
+ *     set_check_indices switch), at the cost of a device-to-host copy.
+ *   - Slots are int32: a cache with num_blocks * block_size above INT32_MAX is
+ *     refused (PKV_ERR_UNSUPPORTED).
  *   - Launch failures return PKV_ERR_HIP.
  */
 #ifndef PKV_H
@@ -109,7 +113,10 @@ typedef struct {
  * for i < n ("KVCache optimisation skill", section 3.1; the framework's
  * prepare_slot_mapping of the KV Cache management design document).
  * block_table: [batch, max_blocks_per_seq]; batch_idx, pos, slots_out: [n].
- * A negative pos gives slot -1 (a row kv_cache_write skips). */
+ * A negative pos gives slot -1 (a row kv_cache_write skips).  The arithmetic is
+ * int32: every block id read must keep id * block_size + block_size <= INT32_MAX,
+ * which holds for any id below the num_blocks of a cache the other entry points
+ * accept. */
 pkv_status pkv_resolve_slots(const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
                              int32_t block_size, const int32_t* batch_idx, const int32_t* pos,
                              int32_t n, int32_t* slots_out, void* stream);
@@ -177,9 +184,10 @@ size_t paged_attn_decode_workspace(const pkv_attn_params* params, const pkv_page
  *                  this step (the query sits at position seq_lens[b]-1); 0 gives a zero row
  *   out          : [batch, H, head_dim] in params->out_dtype
  *   workspace    : >= paged_attn_decode_workspace(params, cache) bytes of device memory
- * With a window, table entries for blocks wholly before the window are never read
- * (they may hold the null block, as the KV Cache management design document's
- * sliding-window manager lays them out). */
+ * Table entries of blocks that hold no visible key -- wholly before the window,
+ * or past the block of key seq_lens[b]-1 -- are never used as block ids, so they
+ * may hold anything: the null block, as the KV Cache management design
+ * document's sliding-window manager lays them out, or an invalid id such as -1. */
 pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_cache* cache,
                              const int32_t* block_table, const int32_t* seq_lens,
                              const pkv_attn_params* params, void* out, void* workspace,
@@ -203,13 +211,20 @@ size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_pag
  *   cu_seqlens_q : [batch + 1], cu[0] = 0, cu[batch] = total_q, n_b = cu[b+1] - cu[b] >= 0
  *   seq_lens_kv  : [batch], cached + new keys (n_b <= seq_lens_kv[b]); the new rows
  *                  must already be in the cache (kv_cache_write first)
- *   max_q_len    : an upper bound of every n_b (sizes the grid)
+ *   max_q_len    : an upper bound of every n_b (it sizes the grid).  The host
+ *                  checks what it can see -- 0 < max_q_len <= total_q and
+ *                  max_q_len * batch >= total_q when total_q > 0, else
+ *                  PKV_ERR_INVALID_ARG -- but the n_b themselves are device
+ *                  contents: a sequence with more rows than max_q_len leaves
+ *                  the rows past it unwritten, like any other malformed index.
  *   out          : [total_q, H, head_dim] in params->out_dtype
  * Standard caches need bf16 and head_dim 64 or 128, and a workspace of the size
  * paged_attn_prefill_workspace gives (PKV_ERR_WORKSPACE otherwise).  MLA caches (absorbed form,
  * the same constraints as decode) also cover multi-token decode (n_b of 2-4):
  * every query row is computed over all the keys it sees by one workgroup, so
- * no workspace is used and a row may span at most 1024 table blocks. */
+ * no workspace is used and a row may span at most 1024 table blocks.  Table
+ * entries of blocks that hold no key visible to any row of the sequence are
+ * never used as block ids (see paged_attn_decode). */
 pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged_cache* cache,
                               const int32_t* block_table, const int32_t* cu_seqlens_q,
                               const int32_t* seq_lens_kv, int32_t total_q, int32_t max_q_len,

@@ -98,7 +98,15 @@ pkv_status pkv_kvm_prepare_block_table(const pkv_kv_manager* m, int32_t group, c
 
 /* ---- sizing (section 4.2.1); each result counts the null block --------------------- */
 
-/* Sliding window: max_concurrency * (ceil((W + 2 next_n) / block_size) + 1) + 1. */
+/* Sliding window: max_concurrency * (ceil((W + 2 next_n) / block_size) + 1) + 1.
+ * This covers the decode steady state.  A fresh prompt chunk of P tokens takes a
+ * real block for every one of its tokens during its step (each new query reads its
+ * keys from the cache, so all of the chunk is written first), i.e.
+ * ceil((P + 2 next_n) / block_size) blocks, and only the next step returns the ones
+ * before the window.  A pool that admits one such chunk at a time therefore needs
+ * this figure plus max(0, ceil((P + 2 next_n) / block_size) - peak) blocks, peak =
+ * ceil((W + 2 next_n - 1) / block_size) + 1 being the most blocks a window touches;
+ * several chunks in flight need that excess once per chunk. */
 pkv_status pkv_block_num_fixed(int32_t max_concurrency, int32_t sliding_window, int32_t next_n,
                                int32_t block_size, int64_t* num_blocks);
 /* Full attention, fixed maximum length: ceil(max_len / block_size) * max_concurrency + 1. */

@@ -9,6 +9,12 @@ missing, ``load()`` raises.
 Names follow the C ABI: ``pkv_resolve_slots``, ``kv_cache_write``,
 ``kv_rmsnorm_rope_cache``, ``paged_attn_decode``, ``paged_attn_prefill`` (+ their
 ``*_workspace`` sizes).
+
+``set_check_indices(True)`` turns on host-side bounds checks of the device index
+arrays (``checks.py``): each call then copies block_table / seq_lens /
+cu_seqlens_q / slot_mapping to the host and raises ``PkvError`` naming the first
+entry a kernel would read out of bounds, before launching anything.  It
+synchronises, so it is a debugging mode (and cannot run under graph capture).
 """
 from __future__ import annotations
 
@@ -55,6 +61,25 @@ class AttnParams(ctypes.Structure):
 
 
 _lib = None
+_check_indices = False
+
+
+def set_check_indices(on: bool) -> None:
+    """Turn the host-side index checks of every entry point on or off (off by default)."""
+    global _check_indices
+    _check_indices = bool(on)
+
+
+def check_indices_enabled() -> bool:
+    return _check_indices
+
+
+def _run_check(fn, *args, **kw) -> None:
+    from . import checks
+    try:
+        fn(*args, **kw)
+    except checks.IndexCheckError as e:
+        raise PkvError(1, f"index check: {e}") from None
 
 
 def load(path: str = LIB_PATH):
@@ -176,6 +201,9 @@ def pkv_resolve_slots(block_table: torch.Tensor, block_size: int, batch_idx: tor
         raise ValueError("block_table must be [batch, max_blocks_per_seq]")
     _expect(pos, (n,), "pos")
     _expect(slots_out, (n,), "slots_out")
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_resolve, bt, block_size, batch_idx, pos)
     if slots_out is None:
         slots_out = torch.empty(n, dtype=torch.int32, device=bt.device)
     _check(load().pkv_resolve_slots(_ptr(bt), bt.shape[0], bt.shape[1], block_size,
@@ -194,6 +222,9 @@ def paged_resolve_slots(block_table: torch.Tensor, block_size: int, batch_idx: t
         raise ValueError("block_table must be [batch, max_blocks_per_seq]")
     _expect(pos, (n,), "pos")
     _expect(slots_out, (n,), "slots_out")
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_resolve, bt, block_size, batch_idx, pos)
     if slots_out is None:
         slots_out = torch.empty(n, dtype=torch.int32, device=bt.device)
     _check(load().paged_resolve_slots(_ptr(bt), bt.shape[1], block_size, _ptr(_i32(batch_idx)),
@@ -213,6 +244,9 @@ def kv_cache_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: Optional[torc
         _expect(k_rope, (n, hkv, cache.k_rope_cache.shape[3]), "k_rope")
     _check_elems(cache, k, v, k_rope)
     d = cache.desc()
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_slots, slot_mapping, d.num_blocks * d.block_size)
     _check(load().kv_cache_write(_ptr(_i32(slot_mapping)), slot_mapping.numel(), _ptr(k), _ptr(v),
                                  _ptr(k_rope), ctypes.byref(d), _stream(stream)))
 
@@ -234,6 +268,9 @@ def kv_rmsnorm_rope_cache(latent: torch.Tensor, gamma: torch.Tensor, cos: torch.
     for t in (latent, gamma, cos, sin, k_nope_out, k_rope_out):
         if t is not None and t.dtype != cache.k_cache.dtype:
             raise TypeError("every array must have the cache dtype")
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_slots, slot_mapping, d.num_blocks * d.block_size)
     _check(load().kv_rmsnorm_rope_cache(_ptr(latent), _ptr(gamma), _ptr(cos), _ptr(sin), _ptr(_i32(slot_mapping)), n,
                                         float(eps), rope_layout, ctypes.byref(d), _ptr(k_nope_out), _ptr(k_rope_out),
                                         _stream(stream)))
@@ -276,6 +313,9 @@ def paged_attn_decode(q: torch.Tensor, cache: PagedKVCache, block_table: torch.T
         out = torch.empty((B, H, D), dtype=out_dtype or q.dtype, device=q.device)
     d = cache.desc()
     p = _params(B, H, block_table, scale, window, _dtype_code(out), split_tokens)
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_decode, block_table, seq_lens, d.block_size, d.num_blocks, int(window))
     lib = load()
     need = int(lib.paged_attn_decode_workspace(ctypes.byref(p), ctypes.byref(d)))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -295,20 +335,30 @@ def paged_attn_prefill_workspace(cache: PagedKVCache, batch: int, num_q_heads: i
 
 
 def paged_attn_prefill(q: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,
-                       cu_seqlens_q: torch.Tensor, seq_lens_kv: torch.Tensor, max_q_len: int,
+                       cu_seqlens_q: torch.Tensor, seq_lens_kv: torch.Tensor, max_q_len: Optional[int],
                        scale: float, window: int = 0, q_rope: Optional[torch.Tensor] = None,
                        out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """q TND [T, H, D] -> out [T, H, D], bottom-right causal over each sequence's keys."""
+    """q TND [T, H, D] -> out [T, H, D], bottom-right causal over each sequence's keys.
+
+    max_q_len must be at least every sequence's row count (it sizes the grid; rows past
+    it would stay unwritten).  None derives it from cu_seqlens_q, which costs a
+    synchronising device-to-host copy when cu_seqlens_q lives on the GPU."""
     T, H, D = q.shape
     B = cu_seqlens_q.numel() - 1
     _check_attn_shapes(cache, q, q_rope, block_table, B, out)
     _expect(seq_lens_kv, (B,), "seq_lens_kv")
     _check_elems(cache, q, q_rope)
+    if max_q_len is None:
+        max_q_len = int(torch.diff(cu_seqlens_q.detach().cpu().long()).max()) if B > 0 else 0
     if out is None:
         out = torch.empty((T, H, D), dtype=out_dtype or q.dtype, device=q.device)
     d = cache.desc()
     p = _params(B, H, block_table, scale, window, _dtype_code(out), 0)
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_prefill, block_table, cu_seqlens_q, seq_lens_kv, T, int(max_q_len),
+                   d.block_size, d.num_blocks, int(window))
     lib = load()
     need = int(lib.paged_attn_prefill_workspace(ctypes.byref(p), ctypes.byref(d), T))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <climits>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -74,6 +75,10 @@ pkv_status check_cache(const pkv_paged_cache* c) {
     return fail(PKV_ERR_UNSUPPORTED, "a rope row is not a multiple of 16 bytes");
   if (!aligned16(c->k_cache) || !aligned16(c->v_cache) || (c->k_rope_cache && !aligned16(c->k_rope_cache)))
     return fail(PKV_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+  // Slots cross the ABI and are resolved on the device as int32.
+  if ((int64_t)c->num_blocks * c->block_size > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "num_blocks %d x block_size %d slots exceed the int32 slot range", c->num_blocks,
+                c->block_size);
   if (is_int8(c)) {
     if (!c->k_scale || !c->v_scale) return fail(PKV_ERR_INVALID_ARG, "int8 cache: k_scale / v_scale is NULL");
     if (!aligned16(c->k_scale) || !aligned16(c->v_scale))
@@ -150,17 +155,6 @@ bool use_stream_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
 }
 
 constexpr int32_t kMaxBpp = 1024;
-
-// Tuning override for the MLA kernel's waves per workgroup (PKV_MLA_WAVES = 1, 2,
-// 4 or 8; unset = the library's choice).  Read once per process.
-int32_t mla_waves_override() {
-  static const int32_t v = [] {
-    const char* e = std::getenv("PKV_MLA_WAVES");
-    const int x = e ? std::atoi(e) : 0;
-    return (x == 1 || x == 2 || x == 4 || x == 8) ? x : 0;
-  }();
-  return v;
-}
 
 DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
   DecodePlan plan{};
@@ -424,7 +418,6 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
     m.window = params->window;
     m.scale_log2e = params->scale * pkv::kLog2e;
     m.out_dtype = params->out_dtype;
-    m.waves_per_group = mla_waves_override();
     m.rows = params->batch;
     hipError_t e = pkv::launch_mla_decode(m, st);
     if (e != hipSuccess) return from_hip(e, "MLA decode launch");
@@ -497,6 +490,17 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
   s = check_params(params, cache);
   if (s) return s;
   if (total_q < 0 || max_q_len < 0) return fail(PKV_ERR_INVALID_ARG, "total_q and max_q_len must be >= 0");
+  // max_q_len sizes the grid: rows past it would never be computed.  The bound
+  // itself lives in device memory (cu_seqlens_q); what the host can check is
+  // that it is not impossible for these totals.
+  if (params->batch > 0 && total_q > 0) {
+    if (max_q_len == 0) return fail(PKV_ERR_INVALID_ARG, "max_q_len is 0 but total_q is %d", total_q);
+    if ((int64_t)max_q_len * params->batch < total_q)
+      return fail(PKV_ERR_INVALID_ARG, "max_q_len %d x batch %d is below total_q %d: some sequence has more rows",
+                  max_q_len, params->batch, total_q);
+    if (max_q_len > total_q)
+      return fail(PKV_ERR_INVALID_ARG, "max_q_len %d exceeds total_q %d", max_q_len, total_q);
+  }
   if (params->split_tokens != 0) return fail(PKV_ERR_INVALID_ARG, "split_tokens applies to decode only");
   if (is_int8(cache)) return fail(PKV_ERR_UNSUPPORTED, "prefill does not read int8 caches");
   if (params->batch == 0 || total_q == 0) return ok();
@@ -533,7 +537,6 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
     m.window = params->window;
     m.scale_log2e = params->scale * pkv::kLog2e;
     m.out_dtype = params->out_dtype;
-    m.waves_per_group = mla_waves_override();
     m.cu_seqlens_q = cu_seqlens_q;
     m.rows = total_q;
     return from_hip(pkv::launch_mla_decode(m, static_cast<hipStream_t>(stream)), "MLA prefill launch");

@@ -373,8 +373,13 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
           load_lds16(vcache8 + slot * row_bytes + head_off + v_src8[i & 1], vdst + 1024 * i);
         }
         if (lane < 16) {
-          const int j = t0 + key;  // the lane's 4 keys lie in one 16-key block
-          const int32_t phys = (j >> bs_log2) == blk ? e0 : e1;
+          // The lane's 4 keys lie in one 16-key block.  A block wholly before the
+          // window start has a table entry that may hold anything (the null
+          // block, or no block id at all): its lanes read the other block's
+          // scales instead, which hold a visible key and are masked like the rest.
+          const int j = t0 + key;
+          const bool blk_visible = ((blk + 1) << bs_log2) > c.lo;
+          const int32_t phys = ((j >> bs_log2) == blk && blk_visible) ? e0 : e1;
           load_lds16(scale_src + ((((int64_t)phys * Hkv + g) << bs_log2) + (j & bs_mask)), sdst);
         }
       }

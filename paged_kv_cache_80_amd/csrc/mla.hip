@@ -326,7 +326,7 @@ hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream) {
   if (a.batch == 0 || a.rows == 0) return hipSuccess;
   if (a.blocks_per_part > kMaxBpp) return hipErrorInvalidValue;
   // Up to 8 waves (128 heads) per workgroup; the head groups tile H exactly.
-  int nw = a.waves_per_group > 0 ? a.waves_per_group : 8;
+  int nw = 8;
   while (tiles16 % nw) nw >>= 1;
   // Query rows go in launches of at most 65528 (the grid's z limit, rounded
   // down to a multiple of 8); prefill pads each launch to a multiple of 8

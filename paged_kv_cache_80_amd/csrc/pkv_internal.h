@@ -145,7 +145,6 @@ struct MlaArgs {
   int32_t max_blocks_per_seq, block_size_log2, blocks_per_part, max_np, window;
   float scale_log2e;
   int32_t out_dtype;
-  int32_t waves_per_group;  // 16-head waves per workgroup (0 = up to 8)
   const int32_t* cu_seqlens_q;  // prefill: [batch + 1] row offsets of the sequences; decode: null
   int32_t rows;                 // query rows: batch (decode) or total_q (prefill)
   int32_t row0;                 // first row of this launch (set by launch_mla_decode)

@@ -148,6 +148,32 @@ def test_prefill_workspace_of_the_key_split(lib):
     assert lib.paged_attn_prefill_workspace(ctypes.byref(big), ctypes.byref(_cache(num_kv_heads=8)), 4096) == 0
 
 
+@pytest.mark.parametrize("total_q,max_q_len,needle", [
+    (8, 0, "max_q_len is 0"),         # a grid sized 0 would leave every row unwritten
+    (8, 3, "below total_q"),          # 3 rows x 2 sequences cannot hold 8 rows
+    (8, 9, "exceeds total_q"),        # no sequence can have more rows than the call
+    (8, -1, ">= 0"),
+])
+def test_prefill_rejects_impossible_max_q_len(lib, total_q, max_q_len, needle):
+    """max_q_len sizes the prefill grid; the host refuses values no cu_seqlens_q can match."""
+    c, p = _cache(), _params(batch=2)
+    rc = lib.paged_attn_prefill(FAKE, None, ctypes.byref(c), FAKE, FAKE, FAKE, total_q, max_q_len, ctypes.byref(p),
+                                FAKE, None, 0, None)
+    assert rc == 1
+    assert needle in lib.pkv_last_error().decode()
+
+
+def test_slot_range_must_fit_int32(lib):
+    """Slots are int32 across the ABI: a pool of more than 2^31 - 1 slots is refused by every
+    entry point that takes a cache (before any launch)."""
+    big = _cache(num_blocks=2**24, block_size=128, num_kv_heads=1, head_dim=64)  # 2^31 slots
+    assert _decode(lib, big, _params()) == 2
+    assert "int32" in lib.pkv_last_error().decode()
+    assert lib.kv_cache_write(FAKE, 4, FAKE, FAKE, None, ctypes.byref(big), None) == 2
+    ok = _cache(num_blocks=2**24 - 1, block_size=128, num_kv_heads=1, head_dim=64)
+    assert lib.kv_cache_write(FAKE, 0, FAKE, FAKE, None, ctypes.byref(ok), None) == 0
+
+
 def test_write_rejects_malformed_arguments(lib):
     c = _cache()
     assert lib.kv_cache_write(FAKE, 4, FAKE, None, None, ctypes.byref(c), None) == 1  # v missing

@@ -132,6 +132,9 @@ def test_int8_full_size(orc, name):
     for sl in live[:64]:
         assert np.array_equal(gks[sl // bs, :, sl % bs].view(np.uint32), ks[sl // bs, :, sl % bs].view(np.uint32))
     assert_rows_close(out, ref, BF16_TOL, rows=units)
+    out32 = d.attend(out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_rows_close(out32, ref, ACC_TOL, rows=units)
 
 
 def test_int8_rejections():

@@ -127,6 +127,9 @@ def test_prefill_full_size_sampled(orc):
     np.testing.assert_array_equal(host(slots), slots_ref)
     assert np.all(np.isfinite(as_f64(out)))
     assert_rows_close(out, ref, BF16_TOL, rows=units)
+    out32 = d.attend(out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_rows_close(out32, ref, ACC_TOL, rows=units)
 
 
 # --------------------------------------------------------------------------- MLA absorbed decode
@@ -191,6 +194,9 @@ def test_mla_full_size_sampled(orc):
     np.testing.assert_array_equal(host(slots), slots_ref)
     assert np.all(np.isfinite(as_f64(out)))
     assert_rows_close(out, ref, BF16_TOL, rows=units)
+    out32 = d.attend(out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_rows_close(out32, ref, ACC_TOL, rows=units)
 
 
 # --------------------------------------------------------------------------- MLA absorbed prefill

@@ -1,0 +1,66 @@
+"""Seeded random parity sweeps (shapes from tests/sweep_cases.py).
+
+CPU: the oracle against the numpy brute force on 150 tiny decode and 100 tiny prefill
+draws -- block sizes 4 / 16 / 128, MHA, GQA, MQA and MLA, windows including 1 and
+windows that cover every key, empty sequences, random pools and tables.
+GPU: 96 small calls of every kernel family through the C ABI against the oracle at the
+bars of the parity tests, stopping at the first mismatch with the case named."""
+import numpy as np
+import pytest
+
+import brute
+import sweep_cases
+from helpers import oracle_run
+
+
+@pytest.mark.parametrize("chunk", range(5))
+def test_oracle_matches_brute_force_on_random_decode(orc, chunk):
+    for i in range(30 * chunk, 30 * chunk + 30):
+        name, c = sweep_cases.tiny_decode(i)
+        out, cc, _ = oracle_run(orc, c)
+        want = brute.decode(cc, cc.k_cache, cc.v_cache_or_k, cc.k_rope_cache)
+        np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-13, err_msg=name)
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_oracle_matches_brute_force_on_random_prefill(orc, chunk):
+    for i in range(25 * chunk, 25 * chunk + 25):
+        name, c = sweep_cases.tiny_prefill(i)
+        out, cc, _ = oracle_run(orc, c)
+        want = brute.prefill(cc, cc.k_cache, cc.v_cache_or_k, cc.k_rope_cache)
+        np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-13, err_msg=name)
+
+
+def test_sweeps_reach_the_edge_cases():
+    """The draws do contain what they are for."""
+    dec = [sweep_cases.tiny_decode(i)[1] for i in range(150)]
+    assert any((c.seq_lens == 0).any() for c in dec)
+    assert any(c.window == 1 for c in dec)
+    assert any(c.window >= int(c.seq_lens.max(initial=0)) for c in dec if c.window)
+    assert {c.block_size for c in dec} == {4, 16, 128}
+    assert any(c.rope_dim for c in dec) and any(c.G > 1 for c in dec) and any(c.Hkv == 1 and c.H > 1 for c in dec)
+    gpu = [sweep_cases.gpu_case(i)[1] for i in range(96)]
+    assert any(c.int8 for c in gpu) and any(c.kind == "prefill" and c.rope_dim for c in gpu)
+
+
+@pytest.mark.gpu
+def test_kernels_match_oracle_on_random_calls(orc):
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gpu_util import DeviceCase, assert_rows_close
+    for i in range(96):
+        name, c, split = sweep_cases.gpu_case(i)
+        print(name, flush=True)
+        ref, _, _ = oracle_run(orc, c)
+        if c.kind == "decode":
+            out, _ = DeviceCase(c).run(out_dtype=torch.float32, split_tokens=split)
+        else:
+            out, _ = DeviceCase(c).run(out_dtype=torch.float32)
+        try:
+            assert_rows_close(out, ref, 1e-5 if c.dtype == "f32" else 1e-4)
+            if c.dtype == "bf16":
+                out, _ = DeviceCase(c).run(split_tokens=split) if c.kind == "decode" else DeviceCase(c).run()
+                assert_rows_close(out, ref, 2e-3)
+        except AssertionError as e:
+            raise AssertionError(f"{name}: {e}") from None
