@@ -193,6 +193,23 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
                              const pkv_attn_params* params, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc: paged_attn_decode with no workspace
+ * argument.  Its scratch space (the partial outputs of the split) is a
+ * library-owned device array of paged_attn_decode_noalloc_capacity() bytes
+ * (32 MiB) per GPU, set up on the first call on each device and held until the
+ * process ends; nothing is allocated or freed per call.  Same arguments, results
+ * and errors as paged_attn_decode, plus PKV_ERR_UNSUPPORTED when the call needs
+ * more scratch than the array holds (paged_attn_decode_workspace gives the need).
+ * Every call on one GPU shares that GPU's array and no call clears it (no kernel
+ * reads scratch it has not written in the same call), so calls that overlap on
+ * one GPU -- on different streams, or from different threads -- race: order them
+ * on one stream. */
+pkv_status paged_attn_decode_noalloc(const void* q, const void* q_rope, const pkv_paged_cache* cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const pkv_attn_params* params, void* out, void* stream);
+size_t paged_attn_decode_noalloc_capacity(void);
+
 /* Bytes of workspace paged_attn_prefill needs (0 when the call is not split).
  * Standard caches: when the (sequence, KV head, 128-column) workgroups of the call
  * are too few to fill the GPU (multi-token decode: a few rows per sequence), the

@@ -35,8 +35,8 @@ STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED", 3: "P
 
 # Every symbol include/pkv.h declares.
 EXPORTS = ("pkv_resolve_slots", "paged_resolve_slots", "kv_cache_write", "kv_rmsnorm_rope_cache", "paged_attn_decode_workspace",
-           "paged_attn_decode", "paged_attn_prefill_workspace", "paged_attn_prefill", "pkv_last_error",
-           "pkv_version")
+           "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_noalloc_capacity",
+           "paged_attn_prefill_workspace", "paged_attn_prefill", "pkv_last_error", "pkv_version")
 
 
 class PkvError(RuntimeError):
@@ -100,11 +100,14 @@ def load(path: str = LIB_PATH):
     lib.paged_attn_decode_workspace.argtypes = [pp, pc]
     lib.paged_attn_decode_workspace.restype = sz
     lib.paged_attn_decode.argtypes = [P, P, pc, P, P, pp, P, P, sz, P]
+    lib.paged_attn_decode_noalloc.argtypes = [P, P, pc, P, P, pp, P, P]
+    lib.paged_attn_decode_noalloc_capacity.argtypes = []
+    lib.paged_attn_decode_noalloc_capacity.restype = sz
     lib.paged_attn_prefill_workspace.argtypes = [pp, pc, i32]
     lib.paged_attn_prefill_workspace.restype = sz
     lib.paged_attn_prefill.argtypes = [P, P, pc, P, P, P, i32, i32, pp, P, P, sz, P]
     for f in (lib.pkv_resolve_slots, lib.paged_resolve_slots, lib.kv_cache_write, lib.kv_rmsnorm_rope_cache, lib.paged_attn_decode,
-              lib.paged_attn_prefill):
+              lib.paged_attn_decode_noalloc, lib.paged_attn_prefill):
         f.restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_version.restype = ctypes.c_char_p
@@ -325,6 +328,31 @@ def paged_attn_decode(q: torch.Tensor, cache: PagedKVCache, block_table: torch.T
                                  _ptr(_i32(seq_lens)), ctypes.byref(p), _ptr(out), _ptr(workspace),
                                  ws_bytes, _stream(stream)))
     return out
+
+
+def paged_attn_decode_noalloc(q: torch.Tensor, cache: PagedKVCache, block_table: torch.Tensor,
+                              seq_lens: torch.Tensor, scale: float, out: torch.Tensor, window: int = 0,
+                              q_rope: Optional[torch.Tensor] = None, split_tokens: int = 0,
+                              stream=None) -> torch.Tensor:
+    """paged_attn_decode for callers that cannot allocate: the caller passes `out`, the split's
+    scratch is the library's static per-GPU array (paged_attn_decode_noalloc_capacity() bytes).
+    Calls that overlap on one GPU race on that array."""
+    B, H, D = q.shape
+    _check_attn_shapes(cache, q, q_rope, block_table, B, out)
+    _expect(seq_lens, (B,), "seq_lens")
+    _check_elems(cache, q, q_rope)
+    d = cache.desc()
+    p = _params(B, H, block_table, scale, window, _dtype_code(out), split_tokens)
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_decode, block_table, seq_lens, d.block_size, d.num_blocks, int(window))
+    _check(load().paged_attn_decode_noalloc(_ptr(q), _ptr(q_rope), ctypes.byref(d), _ptr(_i32(block_table)),
+                                            _ptr(_i32(seq_lens)), ctypes.byref(p), _ptr(out), _stream(stream)))
+    return out
+
+
+def paged_attn_decode_noalloc_capacity() -> int:
+    return int(load().paged_attn_decode_noalloc_capacity())
 
 
 def paged_attn_prefill_workspace(cache: PagedKVCache, batch: int, num_q_heads: int, max_blocks_per_seq: int,

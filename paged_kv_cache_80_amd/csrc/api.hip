@@ -7,6 +7,7 @@
 #include <climits>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "device_common.h"
@@ -246,6 +247,37 @@ PrefillPlan plan_prefill(const pkv_attn_params* p, const pkv_paged_cache* c, int
   return plan;
 }
 
+// Scratch for callers that cannot allocate (paged_attn_decode_noalloc): one
+// library-owned array per GPU, alive until the process ends.  In host code the
+// array's name is only a stand-in; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+pkv_status static_scratch_ptr(void** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDev] = {};
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDev) return fail(PKV_ERR_UNSUPPORTED, "device %d is past the %d the library tracks", dev, kMaxDev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess) return from_hip(g, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(PKV_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return PKV_OK;
+}
+
+pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache* cache, const int32_t* block_table,
+                       const int32_t* seq_lens, const pkv_attn_params* params, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream, bool static_scratch);
+
 }  // namespace
 
 extern "C" {
@@ -373,6 +405,25 @@ size_t paged_attn_decode_workspace(const pkv_attn_params* params, const pkv_page
 pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_cache* cache,
                              const int32_t* block_table, const int32_t* seq_lens, const pkv_attn_params* params,
                              void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, q_rope, cache, block_table, seq_lens, params, out, workspace, workspace_bytes, stream,
+                     false);
+}
+
+pkv_status paged_attn_decode_noalloc(const void* q, const void* q_rope, const pkv_paged_cache* cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     const pkv_attn_params* params, void* out, void* stream) {
+  return decode_impl(q, q_rope, cache, block_table, seq_lens, params, out, nullptr, 0, stream, true);
+}
+
+size_t paged_attn_decode_noalloc_capacity(void) { return kStaticScratchBytes; }
+
+}  // extern "C"
+
+namespace {
+
+pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache* cache, const int32_t* block_table,
+                       const int32_t* seq_lens, const pkv_attn_params* params, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream, bool static_scratch) {
   pkv_status s = check_cache(cache);
   if (s) return s;
   s = check_params(params, cache);
@@ -388,6 +439,14 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
   if (plan.max_np > 65535) return fail(PKV_ERR_UNSUPPORTED, "decode: %d partitions exceed 65535", plan.max_np);
   if ((int64_t)params->batch * cache->num_kv_heads > 0x7fffffff)
     return fail(PKV_ERR_UNSUPPORTED, "decode: batch x num_kv_heads exceeds the grid");
+  if (static_scratch && plan.ws_bytes > 0) {
+    if (plan.ws_bytes > kStaticScratchBytes)
+      return fail(PKV_ERR_UNSUPPORTED, "decode needs %zu bytes of scratch; the library's static array holds %zu",
+                  plan.ws_bytes, kStaticScratchBytes);
+    s = static_scratch_ptr(&workspace);
+    if (s) return s;
+    workspace_bytes = kStaticScratchBytes;
+  }
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -475,6 +534,10 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
   }
   return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache, int32_t total_q) {
   if (check_cache(cache) || check_params(params, cache) || total_q < 0) return 0;
