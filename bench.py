@@ -43,7 +43,9 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mha_decode_7b")
+    ap.add_argument("--workload", default=None,
+                    help="time this workload alone (default: the llama2-7B decode as the headline, then every "
+                         "other configuration of the target list in the 'workloads' map)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split-tokens", type=int, default=0, help="decode partition size (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -51,6 +53,10 @@ def parse_args():
                     help="time the cold-cache steps only (no warm pass, no copy reference), so that a profiler's "
                          "per-kernel averages cover exactly the reported steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--map-steps", type=int, default=20, help="timed steps of each workload in the map")
+    ap.add_argument("--map-cpu-seconds", type=float, default=3.0,
+                    help="target oracle time for each map workload's CPU baseline")
+    ap.add_argument("--no-map", action="store_true", help="time the headline workload only")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the hot path, time a plain device copy of this many MiB (the reference "
                          "for scaling HBM byte counters)")
@@ -381,12 +387,13 @@ def run_latent(args, case, torch, pkv):
         if e1 is not None:
             e1.record()
 
-    ms_step, ms_k, med_k = _timed(torch, step, args)
-    warm = None if args.cold_only else _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), args)
+    ms_step, ms_k, med_k = _timed(torch, step, args.steps, args.warmup)
+    warm = None if args.cold_only else _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), args.steps,
+                                              args.warmup)
     r_b, w_b = latent_bytes(case)
     value = (r_b + w_b) / (ms_step * 1e-3) / 1e9
     k_gbs = w_b / (ms_k * 1e-3) / 1e9
-    result = _result(args, case, value, ms_step, {"workload": case.name, "batch": case.B, "tokens": case.T,
+    result = _result(args, case.name, case.dtype, value, ms_step, {"workload": case.name, "batch": case.B, "tokens": case.T,
                                                   "latent_dim": 512, "rope_dim": 64, "block_size": case.block_size,
                                                   "rope_layout": "half" if case.layout == 0 else "interleaved",
                                                   "returned_rows": case.outputs, "seed": args.seed})
@@ -405,26 +412,26 @@ def run_latent(args, case, torch, pkv):
     print(json.dumps(result), flush=True)
 
 
-def _timed(torch, step, args):
+def _timed(torch, step, steps, warmup):
     """W untimed steps, then K timed steps between synchronisations; returns (ms per step,
     mean ms between each step's two events, their median).  step(i, e0, e1) runs step
     number i."""
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i, (e0, e1) in enumerate(ev):
-        step(args.warmup + i, e0, e1)
+        step(warmup + i, e0, e1)
     end.record()
     torch.cuda.synchronize()
     per = [e0.elapsed_time(e1) for e0, e1 in ev]
-    return start.elapsed_time(end) / args.steps, float(np.mean(per)), float(np.median(per))
+    return start.elapsed_time(end) / steps, float(np.mean(per)), float(np.median(per))
 
 
-def _result(args, case, value, ms_step, config):
+def _result(args, name, dtype, value, ms_step, config):
     return {
         "metric": METRIC,
         "value": round(value, 2),
@@ -436,37 +443,65 @@ def _result(args, case, value, ms_step, config):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": case.dtype,
+        "dtype": dtype,
         "data": "synthetic",
         "config": config,
     }
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path runs "
-              "unsharded on one device", file=sys.stderr)
-        sys.exit(2)
-    import torch
+HEADLINE = "mha_decode_7b"
+# Every other configuration of the target list, timed after the headline into the line's
+# "workloads" map: the tiny fp32 decode (a latency figure), the llama2-70B ragged GQA decode
+# and its window-4096 variant, the chunked prefill and the MLA absorbed decode.
+MAP_WORKLOADS = ("tiny_f32_decode", "gqa_decode_70b", "gqa_decode_70b_window4096", "chunked_prefill", "mla_decode")
 
-    import paged_kv_cache_80_amd as pkv
-    import workloads
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-    if args.copy_calibration_mib:
-        copy_calibration(torch, args.copy_calibration_mib, args.steps)
-        return
-    pkv.load()
+def read_ceiling(torch):
+    """The read bandwidth a plain streaming kernel reaches on this GPU in the same run: 1 GiB
+    read once by libpkv_probe.so (contiguous shares, 16-byte loads, sixteen in flight per
+    lane, 2 workgroups per CU), timed with HIP events on the stream it runs on.  The attainable reference for the
+    HBM-bound calls beside the 8 TB/s datasheet figure."""
+    import ctypes
 
-    case = workloads.WORKLOADS[args.workload](args.seed)
-    case.seed_label = args.seed
-    if case.kind == "latent_write":
-        run_latent(args, case, torch, pkv)
-        return
+    path = os.path.join(ROOT, "paged_kv_cache_80_amd", "libpkv_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m paged_kv_cache_80_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.pkv_probe_sink_words.argtypes = [ctypes.c_int32]
+    lib.pkv_probe_sink_words.restype = ctypes.c_size_t
+    lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.pkv_probe_stream_read.restype = ctypes.c_int
+    n = 1 << 30
+    wgs = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(int(lib.pkv_probe_sink_words(wgs)), dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def launch():
+        if lib.pkv_probe_stream_read(buf.data_ptr(), n, wgs, sink.data_ptr(), st.cuda_stream) != 0:
+            raise RuntimeError("read probe launch failed")
+
+    for _ in range(3):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(st)
+    for _ in range(reps):
+        launch()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"GBps": round(n / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4), "bytes": n,
+            "what": "read-only streaming kernel over 1 GiB (libpkv_probe.so)"}
+
+
+def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass):
+    """Time `steps` steps (resolve -> write -> attention) of one workload after `warmup`
+    untimed ones, on cold-cache copies; returns the result fields of the JSON line."""
     dev = lambda a: _dev(torch, a)  # noqa: E731
     if case.int8:
         cache = int8_cache(torch, pkv, case)
@@ -513,8 +548,8 @@ def main():
         if e1 is not None:
             e1.record()
 
-    ms_step, ms_attn, med_attn = _timed(torch, step, args)
-    warm = None if args.cold_only else _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), args)
+    ms_step, ms_attn, med_attn = _timed(torch, step, steps, warmup)
+    warm = _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), steps, warmup) if warm_pass else None
 
     r_b, w_b, a_b, kv_b = algorithmic_bytes(case)
     flops = algorithmic_flops(case)
@@ -531,30 +566,134 @@ def main():
     else:
         roofline = {"bound": "hbm", "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
-    roofline.update({"traffic": profiled_traffic(args.workload), "kernel": kernel, "bytes_per_launch": a_b,
+    roofline.update({"traffic": profiled_traffic(case.name), "kernel": kernel, "bytes_per_launch": a_b,
                      "flops_per_launch": flops})
-    result = _result(args, case, value, ms_step,
-                     {"workload": case.name, "batch": case.B, "num_q_heads": case.H, "num_kv_heads": case.Hkv,
+    res = {"value": value, "ms_per_step": ms_step, "dtype": case.dtype,
+           "config": {"workload": case.name, "batch": case.B, "num_q_heads": case.H, "num_kv_heads": case.Hkv,
                       "head_dim": case.D, "rope_dim": case.rope_dim, "block_size": case.block_size,
                       "window": case.window, "seq_len_total": int(case.seq_lens.sum()), "seed": args.seed,
-                      "cache": "int8 codes + float32 scale per (token, head)" if case.int8 else case.dtype})
-    result.update({
-        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "tokens_per_s": round(case.new_pos.size / (ms_step * 1e-3), 1),
-        "attention_ms": round(ms_attn, 4),
-        "attention_ms_median": round(med_attn, 4),
-        "attention_GBps": round(attn_gbs, 2),
-        "mfma_util": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": roofline,
-        "cold_cache": {"copies": len(caches), "bytes_per_copy": cache_bytes},
-    })
+                      "cache": "int8 codes + float32 scale per (token, head)" if case.int8 else case.dtype},
+           "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+           "tokens_per_s": round(case.new_pos.size / (ms_step * 1e-3), 1),
+           "attention_ms": round(ms_attn, 4),
+           "attention_ms_median": round(med_attn, 4),
+           "attention_GBps": round(attn_gbs, 2),
+           "mfma_util": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+           "roofline": roofline,
+           "cold_cache": {"copies": len(caches), "bytes_per_copy": cache_bytes}}
     if warm is not None:
-        result["warm"] = {"ms_per_step": round(warm[0], 4), "attention_ms": round(warm[1], 4),
-                          "attention_GBps": round(a_b / (warm[1] * 1e-3) / 1e9, 2),
-                          "mfma_util": round(flops / (warm[1] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        res["warm"] = {"ms_per_step": round(warm[0], 4), "attention_ms": round(warm[1], 4),
+                       "attention_GBps": round(a_b / (warm[1] * 1e-3) / 1e9, 2),
+                       "mfma_util": round(flops / (warm[1] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if a_b < LATENCY_BYTES:
+        res["device_latency"] = backlogged_times(torch, lambda: attend(caches[0]), lambda: step(0))
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(case, cpu_seconds)
+    return res
+
+
+# Calls that move fewer bytes than this are latency-bound: the eager event pair around the
+# call then also holds the host's time to submit it.  Their device time is taken with the
+# stream held back: a spin kernel (torch.cuda._sleep, a fixed number of cycles) runs first
+# while the host queues `reps` calls behind it, so the two events around those calls see
+# only the device executing them back to back.
+LATENCY_BYTES = 64 << 20
+SPIN_CYCLES = 10_000_000
+
+
+def backlogged_times(torch, attend_once, step_once, reps=50):
+    """Microseconds per call of the attention call alone and of the whole step, each queued
+    `reps` times behind a ~10 ms spin kernel and timed between two events."""
+    attend_once()
+    step_once()
+    torch.cuda.synchronize()
+    out = {}
+    for name, fn in (("attention_us", attend_once), ("step_us", step_once)):
+        s0, e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        s0.record()
+        torch.cuda._sleep(SPIN_CYCLES)
+        e0.record()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        e1.record()
+        torch.cuda.synchronize()
+        spin_ms = s0.elapsed_time(e0)
+        if spin_ms <= host_ms:  # the host fell behind: the calls were not queued ahead
+            raise RuntimeError(f"spin of {spin_ms:.2f} ms is shorter than the {host_ms:.2f} ms of submissions")
+        out[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        out[name.replace("_us", "_spin_ms")] = round(spin_ms, 3)
+        out[name.replace("_us", "_host_ms")] = round(host_ms, 3)
+    out["reps"] = reps
+    out["what"] = "calls queued back to back behind a spin kernel, events around them"
+    return out
+
+
+def map_entry(res, ceiling):
+    """The compact record of a workload in the line's "workloads" map."""
+    e = {k: res[k] for k in ("config", "attention_ms", "attention_ms_median", "attention_GBps", "mfma_util",
+                             "tokens_per_s", "roofline", "cold_cache", "device_latency", "cpu_baseline") if k in res}
+    e["ms_per_step"] = round(res["ms_per_step"], 4)
+    e["step_GBps"] = round(res["value"], 2)
+    if "device_latency" in res:  # latency-bound: a time, not a roofline fraction, is the figure
+        e["attention_us"] = res["device_latency"]["attention_us"]
+        e["step_us"] = res["device_latency"]["step_us"]
+    if ceiling and e["roofline"]["bound"] == "hbm":
+        e["roofline"]["frac_of_read_ceiling"] = round(e["roofline"]["achieved"] / ceiling["GBps"], 4)
+    return e
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the path runs "
+              "unsharded on one device", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_80_amd as pkv
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        copy_calibration(torch, args.copy_calibration_mib, args.steps)
+        return
+    pkv.load()
+
+    name = args.workload or HEADLINE
+    case = workloads.WORKLOADS[name](args.seed)
+    case.seed_label = args.seed
+    if case.kind == "latent_write":
+        run_latent(args, case, torch, pkv)
+        return
+    res = measure(args, case, torch, pkv, args.steps, args.warmup,
+                  0.0 if args.no_cpu_baseline else args.cpu_seconds, not args.cold_only)
+    del case
+    result = _result(args, res["config"]["workload"], res["dtype"], res["value"], res["ms_per_step"], res["config"])
+    result.update({k: v for k, v in res.items() if k not in ("value", "ms_per_step", "config", "dtype")})
+    ceiling = None
+    if not args.cold_only:
         result["stream_copy"] = stream_copy_reference(torch)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        ceiling = read_ceiling(torch)
+        result["read_ceiling"] = ceiling
+        if result["roofline"]["bound"] == "hbm":
+            result["roofline"]["frac_of_read_ceiling"] = round(result["roofline"]["achieved"] / ceiling["GBps"], 4)
+    if args.workload is None and not args.no_map:
+        wl = {}
+        for other in MAP_WORKLOADS:
+            print(f"bench: {other}", file=sys.stderr, flush=True)
+            c = workloads.WORKLOADS[other](args.seed)
+            c.seed_label = args.seed
+            r = measure(args, c, torch, pkv, args.map_steps, 3,
+                        0.0 if args.no_cpu_baseline else args.map_cpu_seconds, False)
+            del c
+            torch.cuda.empty_cache()
+            wl[other] = map_entry(r, ceiling)
+        result["workloads"] = wl
     print(json.dumps(result), flush=True)
 
 

@@ -48,6 +48,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(PKG, "libpkv_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """libpkv_probe.so: the read-bandwidth reference bench.py times in the same run (not part
+    of the attention library)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *COMMON, "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
@@ -66,4 +84,5 @@ def build(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)
     sys.exit(0)
