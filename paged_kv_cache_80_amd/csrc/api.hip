@@ -165,7 +165,8 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
     plan.split_tiles = p->split_tokens / 32;  // split_tokens is a multiple of the block size (>= 16)
     if (p->split_tokens > 0 && plan.split_tiles == 0) plan.split_tiles = 1;
     plan.max_np = 1;
-    plan.ws_bytes = pkv::decode_stream_workspace(p->batch, p->num_q_heads, c->num_kv_heads, plan.resident_waves,
+    plan.ws_bytes = pkv::decode_stream_workspace(p->batch, p->num_q_heads / c->num_kv_heads, c->num_kv_heads,
+                                                 plan.resident_waves,
                                                  &plan.ws_o_offset, &plan.ws_ml_offset);
     return plan;
   }
@@ -535,13 +536,40 @@ pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache*
   return ok();
 }
 
+// Multi-token decode (a few query rows per sequence) through the stream split of
+// decode: when every sequence's rows times the head group fit the kernel's two
+// 16-column tiles, its K/V are streamed once for all of them, as in decode.  The
+// call decides from max_q_len; the workspace query, which only sees total_q,
+// answers for both paths whenever the average row count allows this one.
+bool stream_mt_supported(const pkv_attn_params* p, const pkv_paged_cache* c) {
+  if (is_mla(c) || c->dtype != PKV_BF16) return false;
+  const int32_t group = p->num_q_heads / c->num_kv_heads;
+  return pkv::decode_mfma_supported(c->dtype, c->head_dim, group) &&
+         c->num_kv_heads <= pkv::decode_stream_resident_waves(device_cu_count(), c->dtype);
+}
+
+bool stream_mt_fits(const pkv_attn_params* p, const pkv_paged_cache* c, int64_t rows) {
+  return rows > 0 && rows * (p->num_q_heads / c->num_kv_heads) <= pkv::kStreamMtColumns;
+}
+
+size_t stream_mt_workspace(const pkv_attn_params* p, const pkv_paged_cache* c, size_t* o_off, size_t* ml_off) {
+  return pkv::decode_stream_workspace(p->batch, pkv::kStreamMtColumns, c->num_kv_heads,
+                                      pkv::decode_stream_resident_waves(device_cu_count(), c->dtype), o_off, ml_off);
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t paged_attn_prefill_workspace(const pkv_attn_params* params, const pkv_paged_cache* cache, int32_t total_q) {
   if (check_cache(cache) || check_params(params, cache) || total_q < 0) return 0;
-  return plan_prefill(params, cache, total_q).ws_bytes;
+  size_t ws = plan_prefill(params, cache, total_q).ws_bytes;
+  if (params->batch > 0 && stream_mt_supported(params, cache) &&
+      stream_mt_fits(params, cache, ((int64_t)total_q + params->batch - 1) / params->batch)) {
+    size_t o_off, ml_off;
+    ws = std::max(ws, stream_mt_workspace(params, cache, &o_off, &ml_off));
+  }
+  return ws;
 }
 
 pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged_cache* cache,
@@ -604,6 +632,42 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
     m.rows = total_q;
     return from_hip(pkv::launch_mla_decode(m, static_cast<hipStream_t>(stream)), "MLA prefill launch");
   }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (stream_mt_supported(params, cache) && stream_mt_fits(params, cache, max_q_len)) {
+    size_t o_off = 0, ml_off = 0;
+    const size_t need = stream_mt_workspace(params, cache, &o_off, &ml_off);
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    char* wsb = static_cast<char*>(workspace);
+    pkv::DecodeArgs d{};
+    d.q = q;
+    d.k_cache = cache->k_cache;
+    d.v_cache = cache->v_cache;
+    d.block_table = block_table;
+    d.seq_lens = seq_lens_kv;
+    d.out = out;
+    d.ws_o = reinterpret_cast<float*>(wsb + o_off);
+    d.ws_ml = reinterpret_cast<float*>(wsb + ml_off);
+    d.batch = params->batch;
+    d.num_q_heads = params->num_q_heads;
+    d.num_kv_heads = cache->num_kv_heads;
+    d.head_dim = cache->head_dim;
+    d.max_blocks_per_seq = params->max_blocks_per_seq;
+    d.block_size_log2 = log2i(cache->block_size);
+    d.blocks_per_part = 1;
+    d.max_np = 1;
+    d.window = params->window;
+    d.scale_log2e = params->scale * pkv::kLog2e;
+    d.dtype = cache->dtype;
+    d.out_dtype = params->out_dtype;
+    d.tile_prefix = reinterpret_cast<int32_t*>(wsb);
+    d.resident_waves = pkv::decode_stream_resident_waves(device_cu_count(), cache->dtype);
+    d.split_tiles = 0;
+    d.cu_seqlens_q = cu_seqlens_q;
+    d.total_q = total_q;
+    return from_hip(pkv::launch_decode_stream(d, st), "multi-token decode launch");
+  }
   if (params->max_blocks_per_seq > pkv::kPrefillMaxTableBlocks)
     return fail(PKV_ERR_UNSUPPORTED, "prefill: max_blocks_per_seq %d exceeds %d", params->max_blocks_per_seq,
                 pkv::kPrefillMaxTableBlocks);
@@ -637,7 +701,6 @@ pkv_status paged_attn_prefill(const void* q, const void* q_rope, const pkv_paged
   a.window = params->window;
   a.scale_log2e = params->scale * pkv::kLog2e;
   a.out_dtype = params->out_dtype;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = pkv::launch_prefill_mfma(a, st);
   if (e != hipSuccess) return from_hip(e, "prefill launch");
   if (plan.np > 1) {

@@ -84,6 +84,7 @@ struct Geo {
   static constexpr int kDma = I8 ? 9 : 16;
 };
 constexpr int kLdsPrefix = 2048;                   // batch + 1 up to this: prefix scanned in LDS
+constexpr int kStreamCols = kStreamMtColumns;      // columns of a multi-token decode piece (two tiles)
 
 // 16-byte chunk swizzles of row r in the staged K and V tiles.
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
@@ -109,15 +110,20 @@ __device__ __forceinline__ T sload(const T* p) {
   return *(const __attribute__((address_space(4))) T*)(p);
 }
 
-// Visible keys of a sequence of length L: [lo, L), lo = L - W with a window W.
-__device__ __forceinline__ int32_t visible_lo(int32_t L, int32_t window) {
-  return (window > 0 && L > window) ? L - window : 0;
+// Keys some query of a sequence of length L sees, when its last n keys are query
+// rows (n = 1: decode): row i sits at position L - n + i and sees (pos - W, pos]
+// with a window W, so together they see [lo, L), lo = L - n + 1 - W.
+__device__ __forceinline__ int32_t visible_lo(int32_t L, int32_t window, int32_t n) {
+  return (window > 0 && L - n + 1 > window) ? L - n + 1 - window : 0;
 }
-// 32-key tiles covering [lo, L), aligned to absolute positions.
-__device__ __forceinline__ int32_t seq_tiles(int32_t L, int32_t window) {
-  if (L <= 0) return 0;
-  return ((L - 1) >> kTileLog2) - (visible_lo(L, window) >> kTileLog2) + 1;
+// 32-key tiles covering [lo, L), aligned to absolute positions (none without a row).
+__device__ __forceinline__ int32_t seq_tiles(int32_t L, int32_t window, int32_t n) {
+  if (L <= 0 || n <= 0) return 0;
+  return ((L - 1) >> kTileLog2) - (visible_lo(L, window, n) >> kTileLog2) + 1;
 }
+// Query rows of sequence b: one per sequence in decode, n_b from cu_seqlens_q
+// in multi-token decode.
+__device__ __forceinline__ int32_t seq_rows(const int32_t* cu, int32_t b) { return cu ? cu[b + 1] - cu[b] : 1; }
 
 // Wave groups that share the C columns: every resident group, or fewer when a
 // target number of tiles per wave is given (split_tiles > 0), and never more
@@ -136,15 +142,16 @@ __device__ __forceinline__ int64_t group_of_column(int64_t t, int64_t C, int64_t
 
 // prefix[b] = sum of seq_tiles over sequences < b (prefix[B] = all columns).
 // One workgroup of 1024 threads scans 1024 sequences per step.
-__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ seq_lens, int32_t B,
-                                                           int32_t window, int32_t* __restrict__ prefix) {
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ seq_lens,
+                                                           const int32_t* __restrict__ cu, int32_t B, int32_t window,
+                                                           int32_t* __restrict__ prefix) {
   __shared__ int32_t s_scan[1024];
   const int tid = threadIdx.x;
   int32_t run = 0;
   if (tid == 0) prefix[0] = 0;
   for (int32_t base = 0; base < B; base += 1024) {
     const int32_t b = base + tid;
-    s_scan[tid] = b < B ? seq_tiles(seq_lens[b], window) : 0;
+    s_scan[tid] = b < B ? seq_tiles(seq_lens[b], window, seq_rows(cu, b)) : 0;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
       const int32_t add = tid >= off ? s_scan[tid - off] : 0;
@@ -161,8 +168,9 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __rest
 // Position of a wave in the column list: sequence b, tile k of its n tiles.
 struct Cursor {
   int32_t b, k, n;
-  int32_t lo, L;     // visible keys [lo, L) of sequence b
+  int32_t lo, L;     // keys [lo, L) of sequence b that some query row sees
   int32_t t_first;   // first key of tile 0 (lo rounded down to a tile)
+  int32_t nq, q0;    // query rows of sequence b and the first one's index
 };
 
 // ONE_BLOCK: the block size is 32 or more, so a 32-key tile never straddles
@@ -170,10 +178,16 @@ struct Cursor {
 // LDS_PREFIX: every workgroup scans seq_lens into its own LDS copy of the
 // column prefix (batch + 1 <= kLdsPrefix) and workgroup 0 also stores it for
 // the combine; otherwise tile_prefix_kernel has written it to the workspace.
-template <bool ONE_BLOCK, bool LDS_PREFIX, bool I8>
+// MT: multi-token decode -- sequence b has n_b query rows (cu_seqlens_q) at its
+// last n_b positions, each seeing the keys up to its own position (bottom-right
+// causal); the columns of a wave are then the (row, head) pairs of its KV head,
+// row-major, in two 16-column tiles.
+template <bool ONE_BLOCK, bool LDS_PREFIX, bool I8, bool MT>
 __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_stream_kernel(DecodeArgs a) {
   constexpr int KS = kD / 32;  // contraction steps of q.k
   constexpr int DT = kD / 16;  // 16-row tiles of O^T
+  constexpr int CT = MT ? 2 : 1;  // 16-column tiles per wave
+  static_assert(!(MT && I8), "multi-token decode reads bf16 caches");
   constexpr int NW = I8 ? kWavesI8 : kWaves;
   using GT = Geo<I8>;
   __shared__ __attribute__((aligned(16))) unsigned char lds_buf[NW * 2 * GT::kSlot];
@@ -193,14 +207,17 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
     // Thread t owns sequences [kPerThread t, kPerThread (t + 1)): local sums,
     // a wave scan of the thread totals, then the waves' totals through LDS.
     constexpr int kPerThread = kLdsPrefix / (NW * kWave);
-    int32_t incl[kPerThread];
+    int32_t incl[kPerThread], nrow[kPerThread];
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)  // all loads first (clamped: B >= 1), then the sums
-      incl[j] = a.seq_lens[min(kPerThread * tid + j, B - 1)];
+    for (int j = 0; j < kPerThread; ++j) {  // all loads first (clamped: B >= 1), then the sums
+      const int bb = min(kPerThread * tid + j, B - 1);
+      incl[j] = a.seq_lens[bb];
+      nrow[j] = MT ? a.cu_seqlens_q[bb + 1] - a.cu_seqlens_q[bb] : 1;
+    }
     int32_t run = 0;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-      run += kPerThread * tid + j < B ? seq_tiles(incl[j], a.window) : 0;
+      run += kPerThread * tid + j < B ? seq_tiles(incl[j], a.window, nrow[j]) : 0;
       incl[j] = run;
     }
     int32_t x = run;  // inclusive scan of the thread totals over the wave
@@ -251,7 +268,9 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
     c0.n = prefix_at(lo_b + 1) - p0;
     c0.k = (int)(c_beg - p0);
     c0.L = sload(a.seq_lens + c0.b);
-    c0.lo = visible_lo(c0.L, a.window);
+    c0.q0 = MT ? sload(a.cu_seqlens_q + c0.b) : c0.b;
+    c0.nq = MT ? sload(a.cu_seqlens_q + c0.b + 1) - c0.q0 : 1;
+    c0.lo = visible_lo(c0.L, a.window, c0.nq);
     c0.t_first = c0.lo & ~(kKeyTile - 1);
   }
   auto advance = [&](Cursor& c) {
@@ -263,7 +282,9 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
     } while (c.n == 0);
     if (c.b < B) {
       c.L = sload(a.seq_lens + c.b);
-      c.lo = visible_lo(c.L, a.window);
+      c.q0 = MT ? sload(a.cu_seqlens_q + c.b) : c.b;
+      c.nq = MT ? sload(a.cu_seqlens_q + c.b + 1) - c.q0 : 1;
+      c.lo = visible_lo(c.L, a.window, c.nq);
       c.t_first = c.lo & ~(kKeyTile - 1);
     }
   };
@@ -417,40 +438,65 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
     }
   };
 
-  const bool cvalid = l16 < G;
+  // Column l16 of tile ct: query head g G + l16 (decode), or (row, head) pair
+  // 16 ct + l16 of the sequence's rows x G heads (multi-token decode), whose row
+  // sits at position cpos.
+  bool cvalid[CT];
+  int32_t cpos[CT];
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
-  uint4 qf[KS];
+  uint4 qf[CT][KS];
   auto load_q = [&](const Cursor& c) {
-    const int64_t qrow = (int64_t)c.b * H + (int64_t)g * G + l16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = I8 ? 16 * (lg + 4 * (ks >> 1)) + 8 * (ks & 1) : 32 * ks + 8 * lg;
-      qf[ks] = cvalid ? ld16(qp + qrow * kD + d0) : make_uint4(0, 0, 0, 0);
+    for (int ct = 0; ct < CT; ++ct) {
+      int64_t qrow;
+      if constexpr (MT) {
+        const int col = 16 * ct + l16;
+        const int i = col / G;
+        cvalid[ct] = i < c.nq;
+        cpos[ct] = c.L - c.nq + i;
+        qrow = (int64_t)(c.q0 + (cvalid[ct] ? i : 0)) * H + (int64_t)g * G + (col - i * G);
+      } else {
+        cvalid[ct] = l16 < G;
+        cpos[ct] = c.L - 1;
+        qrow = (int64_t)c.q0 * H + (int64_t)g * G + l16;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int d0 = I8 ? 16 * (lg + 4 * (ks >> 1)) + 8 * (ks & 1) : 32 * ks + 8 * lg;
+        qf[ct][ks] = cvalid[ct] ? ld16(qp + qrow * kD + d0) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
 
-  f32x4_t o[DT];
-  float mref, l;  // column reference maximum (log2 units), lane partial sum
+  f32x4_t o[CT][DT];
+  float mref[CT], l[CT];  // column reference maximum (log2 units), lane partial sum
   auto reset = [&] {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_zero();
-    mref = kNegInf;
-    l = 0.f;
-  };
-  // Store the partial of the piece of sequence c.b held, as piece (grp + b) H_kv + g.
-  auto flush = [&](const Cursor& c) {
-    const float lsum = row4_sum(l);
-    if (!cvalid) return;
-    const int64_t prow = ((grp + c.b) * Hkv + g) * G + l16;
-    float* wo = a.ws_o + prow * kD;
+    for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const float v[4] = {o[dt][0], o[dt][1], o[dt][2], o[dt][3]};
-      store4(wo, 16 * dt + 4 * lg, v, PKV_F32);
+      for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4_zero();
+      mref[ct] = kNegInf;
+      l[ct] = 0.f;
     }
-    if (lg == 0) {
-      a.ws_ml[prow * 2 + 0] = mref;
-      a.ws_ml[prow * 2 + 1] = lsum;
+  };
+  // Store the partial of the piece of sequence c.b held, as piece (grp + b) H_kv + g
+  // (kStreamCols columns of a piece in multi-token decode, G in decode).
+  auto flush = [&](const Cursor& c) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const float lsum = row4_sum(l[ct]);
+      if (!cvalid[ct]) continue;
+      const int64_t prow = MT ? ((grp + c.b) * Hkv + g) * kStreamCols + 16 * ct + l16 : ((grp + c.b) * Hkv + g) * G + l16;
+      float* wo = a.ws_o + prow * kD;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float v[4] = {o[ct][dt][0], o[ct][dt][1], o[ct][dt][2], o[ct][dt][3]};
+        store4(wo, 16 * dt + 4 * lg, v, PKV_F32);
+      }
+      if (lg == 0) {
+        a.ws_ml[prow * 2 + 0] = mref[ct];
+        a.ws_ml[prow * 2 + 1] = lsum;
+      }
     }
   };
 
@@ -468,8 +514,8 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint4 kw = *reinterpret_cast<const uint4*>(kt + kr8_off[u][h]);
-        s[u] = mfma_bf16(i8x8_to_bf16(make_uint2(kw.x, kw.y)), qf[2 * h], h == 0 ? f32x4_zero() : s[u]);
-        s[u] = mfma_bf16(i8x8_to_bf16(make_uint2(kw.z, kw.w)), qf[2 * h + 1], s[u]);
+        s[u] = mfma_bf16(i8x8_to_bf16(make_uint2(kw.x, kw.y)), qf[0][2 * h], h == 0 ? f32x4_zero() : s[u]);
+        s[u] = mfma_bf16(i8x8_to_bf16(make_uint2(kw.z, kw.w)), qf[0][2 * h + 1], s[u]);
       }
     }
     // Lane (n, lg) holds keys 8 lg + 4 u + e of tile u.
@@ -505,15 +551,15 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mt = row4_max(mt);
     const float mts = mt * c2;
-    const bool raise = mts > mref + kRescaleLog2;
+    const bool raise = mts > mref[0] + kRescaleLog2;
     if (__any(raise)) {
-      const float alpha = raise ? exp2_fast(mref - mts) : 1.f;
-      if (raise) mref = mts;
-      l *= alpha;
+      const float alpha = raise ? exp2_fast(mref[0] - mts) : 1.f;
+      if (raise) mref[0] = mts;
+      l[0] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) o[0][dt] *= alpha;
     }
-    const float mb = mref == kNegInf ? 0.f : mref;
+    const float mb = mref[0] == kNegInf ? 0.f : mref[0];
     float pv[8];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -521,7 +567,7 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float p = exp2_fast(fmaf(s[u][e], c2, -mb));
-        l += p;
+        l[0] += p;
         pv[4 * u + e] = p * vs[e];
       }
     }
@@ -530,8 +576,8 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const uint4 af = i8x8_to_bf16(lds_tr8(vt + vr8_off[dt]));
-      o[dt] = mfma_bf16(af, phi, o[dt]);
-      o[dt] = mfma_bf16(af, plo, o[dt]);
+      o[0][dt] = mfma_bf16(af, phi, o[0][dt]);
+      o[0][dt] = mfma_bf16(af, plo, o[0][dt]);
     }
   };
 
@@ -540,55 +586,81 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
     const unsigned char* kt = slots + sl * GT::kSlot;
     const unsigned char* vt = kt + GT::kTile;
 
-    f32x4_t s[2];
+    f32x4_t s[CT][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint4 af = *reinterpret_cast<const uint4*>(kt + kr_off[ks] + u * 16 * kRowBytes);
-        s[u] = mfma_bf16(af, qf[ks], ks == 0 ? f32x4_zero() : s[u]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) s[ct][u] = mfma_bf16(af, qf[ct][ks], ks == 0 ? f32x4_zero() : s[ct][u]);
       }
     }
-    if (!(t0 >= c.lo && t0 + kKeyTile <= c.L)) {
+    if constexpr (MT) {
+      // Column (row at cpos) sees keys (cpos - W, cpos]; a tile every column sees
+      // whole lies at or after the last row's window start and at or before the
+      // first row's position.
+      const int lo_all = a.window > 0 ? max(0, c.L - a.window) : 0;
+      if (!(t0 >= lo_all && t0 + kKeyTile - 1 <= c.L - c.nq)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int j = t0 + 16 * u + 4 * lg + e;
+              const bool vis = j <= cpos[ct] && (a.window == 0 || j > cpos[ct] - a.window);
+              s[ct][u][e] = vis ? s[ct][u][e] : kNegInf;
+            }
+      }
+    } else {
+      if (!(t0 >= c.lo && t0 + kKeyTile <= c.L)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = t0 + 16 * u + 4 * lg + e;
+            s[0][u][e] = (j >= c.lo && j < c.L) ? s[0][u][e] : kNegInf;
+          }
+      }
+    }
+    uint4 phi[CT], plo[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float mt = fmaxf(fmaxf(fmaxf(s[ct][0][0], s[ct][0][1]), fmaxf(s[ct][0][2], s[ct][0][3])),
+                       fmaxf(fmaxf(s[ct][1][0], s[ct][1][1]), fmaxf(s[ct][1][2], s[ct][1][3])));
+      mt = row4_max(mt);
+      const float mts = mt * c2;
+      const bool raise = mts > mref[ct] + kRescaleLog2;
+      if (__any(raise)) {
+        const float alpha = raise ? exp2_fast(mref[ct] - mts) : 1.f;  // mref = -inf gives 0
+        if (raise) mref[ct] = mts;
+        l[ct] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+      }
+      const float mb = mref[ct] == kNegInf ? 0.f : mref[ct];  // no finite logit yet: every p is 0
+      float p8[8];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int j = t0 + 16 * u + 4 * lg + e;
-          s[u][e] = (j >= c.lo && j < c.L) ? s[u][e] : kNegInf;
+          const float p = exp2_fast(fmaf(s[ct][u][e], c2, -mb));
+          p8[4 * u + e] = p;
+          l[ct] += p;
         }
+      pack_p_split(p8, phi[ct], plo[ct]);
     }
-    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mt = row4_max(mt);
-    const float mts = mt * c2;
-    const bool raise = mts > mref + kRescaleLog2;
-    if (__any(raise)) {
-      const float alpha = raise ? exp2_fast(mref - mts) : 1.f;  // mref = -inf gives 0
-      if (raise) mref = mts;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-    const float mb = mref == kNegInf ? 0.f : mref;  // no finite logit yet: every p is 0
-    float p8[8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = exp2_fast(fmaf(s[u][e], c2, -mb));
-        p8[4 * u + e] = p;
-        l += p;
-      }
-    uint4 phi, plo;
-    pack_p_split(p8, phi, plo);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const uint2 x0 = lds_tr16(reinterpret_cast<const uint16_t*>(vt + vr_off[dt]));
       const uint2 x1 = lds_tr16(reinterpret_cast<const uint16_t*>(vt + vr_off[dt] + 16 * kRowBytes));
       const uint4 af = make_uint4(x0.x, x0.y, x1.x, x1.y);
-      o[dt] = mfma_bf16(af, phi, o[dt]);
-      o[dt] = mfma_bf16(af, plo, o[dt]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        o[ct][dt] = mfma_bf16(af, phi[ct], o[ct][dt]);
+        o[ct][dt] = mfma_bf16(af, plo[ct], o[ct][dt]);
+      }
     }
   };
 
@@ -627,20 +699,35 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
   flush(cc);
 }
 
-// One wave per output row (sequence b, query head h): merge the pieces of
-// (b, h / G): M = max m_p, L = sum l_p 2^(m_p - M), out = sum o_p 2^(m_p - M) / L.
-// Lanes read the (m, l) of up to 64 pieces at once; a sequence with no visible
-// key gets a zero row.
+// One wave per output row (query row t of sequence b, query head h): merge the
+// pieces of (b, h / G): M = max m_p, L = sum l_p 2^(m_p - M), out = sum o_p
+// 2^(m_p - M) / L.  Lanes read the (m, l) of up to 64 pieces at once; a
+// sequence with no visible key gets a zero row.  Decode: t = b and the piece
+// column is h % G; multi-token decode (MT): b holds row t (cu_seqlens_q) and the
+// column is (t - cu[b]) G + h % G.
+template <bool MT>
 __global__ __launch_bounds__(kWaves * kWave) void stream_combine_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int H = a.num_q_heads;
-  if (row >= (int64_t)a.batch * H) return;
-  const int b = (int)(row / H);
+  if (row >= (int64_t)(MT ? a.total_q : a.batch) * H) return;
+  const int t = (int)(row / H);
   const int h = (int)(row % H);
   const int Hkv = a.num_kv_heads;
   const int G = H / Hkv;
-  const int g = h / G, c = h % G;
+  const int g = h / G;
+  int b = t, c = h % G;
+  if constexpr (MT) {
+    const int32_t* cu = a.cu_seqlens_q;
+    int lo_b = 0, hi_b = a.batch - 1;  // the last b with cu[b] <= t
+    while (lo_b < hi_b) {
+      const int mid = (lo_b + hi_b + 1) >> 1;
+      if (cu[mid] <= t) lo_b = mid; else hi_b = mid - 1;
+    }
+    b = lo_b;
+    c += (t - cu[b]) * G;
+  }
+  const int64_t cols = MT ? kStreamCols : G;  // columns of a piece
   const int32_t* prefix = a.tile_prefix;
   const int32_t p0 = prefix[b];
   const int32_t n = prefix[b + 1] - p0;
@@ -651,7 +738,7 @@ __global__ __launch_bounds__(kWaves * kWave) void stream_combine_kernel(DecodeAr
     const int64_t xA = group_of_column(p0, C, NG), xB = group_of_column(p0 + n - 1, C, NG);
     // Groups in [xA, xB] with an empty run (fewer columns than groups) store
     // nothing; every other one holds a piece of sequence b.
-    auto piece_row = [&](int64_t x) { return ((x + b) * Hkv + g) * G + c; };
+    auto piece_row = [&](int64_t x) { return ((x + b) * Hkv + g) * cols + c; };
     float M = kNegInf, Ls = 0.f;
     for (int64_t x0 = xA; x0 <= xB; x0 += kWave) {  // pass 1: the maximum
       const int64_t x = x0 + lane;
@@ -709,9 +796,9 @@ int32_t decode_stream_resident_waves(int32_t cu_count, int32_t dtype) {
   return cu_count * (dtype == PKV_INT8 ? kWavesI8 : kWaves);
 }
 
-size_t decode_stream_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t resident_waves,
+size_t decode_stream_workspace(int32_t batch, int32_t columns, int32_t num_kv_heads, int32_t resident_waves,
                                size_t* ws_o_offset, size_t* ws_ml_offset) {
-  const size_t group = (size_t)(num_q_heads / num_kv_heads);
+  const size_t group = (size_t)columns;
   const size_t pieces = (size_t)resident_waves + (size_t)batch * num_kv_heads;
   const size_t prefix_bytes = (((size_t)batch + 1) * sizeof(int32_t) + 255) & ~size_t(255);
   const size_t o_bytes = (pieces * group * kD * sizeof(float) + 255) & ~size_t(255);
@@ -723,8 +810,10 @@ size_t decode_stream_workspace(int32_t batch, int32_t num_q_heads, int32_t num_k
 hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch <= 0) return hipSuccess;
   const bool lds_prefix = (int64_t)a.batch + 1 <= kLdsPrefix;
+  const bool mt = a.cu_seqlens_q != nullptr;
+  if (mt && a.dtype != PKV_BF16) return hipErrorInvalidValue;
   if (!lds_prefix) {
-    tile_prefix_kernel<<<1, 1024, 0, stream>>>(a.seq_lens, a.batch, a.window, a.tile_prefix);
+    tile_prefix_kernel<<<1, 1024, 0, stream>>>(a.seq_lens, a.cu_seqlens_q, a.batch, a.window, a.tile_prefix);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -732,22 +821,31 @@ hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream) {
   if (a.dtype == PKV_INT8) {
     const unsigned grid = (unsigned)(a.resident_waves / kWavesI8);
     const dim3 blk(kWavesI8 * kWave);
-    if (lds_prefix && one_block) decode_stream_kernel<true, true, true><<<grid, blk, 0, stream>>>(a);
-    else if (lds_prefix) decode_stream_kernel<false, true, true><<<grid, blk, 0, stream>>>(a);
-    else if (one_block) decode_stream_kernel<true, false, true><<<grid, blk, 0, stream>>>(a);
-    else decode_stream_kernel<false, false, true><<<grid, blk, 0, stream>>>(a);
+    if (lds_prefix && one_block) decode_stream_kernel<true, true, true, false><<<grid, blk, 0, stream>>>(a);
+    else if (lds_prefix) decode_stream_kernel<false, true, true, false><<<grid, blk, 0, stream>>>(a);
+    else if (one_block) decode_stream_kernel<true, false, true, false><<<grid, blk, 0, stream>>>(a);
+    else decode_stream_kernel<false, false, true, false><<<grid, blk, 0, stream>>>(a);
+  } else if (mt) {
+    const unsigned grid = (unsigned)(a.resident_waves / kWaves);
+    const dim3 blk(kWaves * kWave);
+    if (lds_prefix && one_block) decode_stream_kernel<true, true, false, true><<<grid, blk, 0, stream>>>(a);
+    else if (lds_prefix) decode_stream_kernel<false, true, false, true><<<grid, blk, 0, stream>>>(a);
+    else if (one_block) decode_stream_kernel<true, false, false, true><<<grid, blk, 0, stream>>>(a);
+    else decode_stream_kernel<false, false, false, true><<<grid, blk, 0, stream>>>(a);
   } else {
     const unsigned grid = (unsigned)(a.resident_waves / kWaves);
     const dim3 blk(kWaves * kWave);
-    if (lds_prefix && one_block) decode_stream_kernel<true, true, false><<<grid, blk, 0, stream>>>(a);
-    else if (lds_prefix) decode_stream_kernel<false, true, false><<<grid, blk, 0, stream>>>(a);
-    else if (one_block) decode_stream_kernel<true, false, false><<<grid, blk, 0, stream>>>(a);
-    else decode_stream_kernel<false, false, false><<<grid, blk, 0, stream>>>(a);
+    if (lds_prefix && one_block) decode_stream_kernel<true, true, false, false><<<grid, blk, 0, stream>>>(a);
+    else if (lds_prefix) decode_stream_kernel<false, true, false, false><<<grid, blk, 0, stream>>>(a);
+    else if (one_block) decode_stream_kernel<true, false, false, false><<<grid, blk, 0, stream>>>(a);
+    else decode_stream_kernel<false, false, false, false><<<grid, blk, 0, stream>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t rows = (int64_t)a.batch * a.num_q_heads;
-  stream_combine_kernel<<<(unsigned)((rows + kWaves - 1) / kWaves), kWaves * kWave, 0, stream>>>(a);
+  const int64_t rows = (int64_t)(mt ? a.total_q : a.batch) * a.num_q_heads;
+  const unsigned cgrid = (unsigned)((rows + kWaves - 1) / kWaves);
+  if (mt) stream_combine_kernel<true><<<cgrid, kWaves * kWave, 0, stream>>>(a);
+  else stream_combine_kernel<false><<<cgrid, kWaves * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 

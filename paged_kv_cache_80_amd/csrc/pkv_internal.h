@@ -82,6 +82,11 @@ struct DecodeArgs {
   // [num_blocks, num_kv_heads, block_size] order.
   const float* k_scale;
   const float* v_scale;
+  // Multi-token decode through the stream split (bf16): the rows of sequence b
+  // are q rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 at its last positions;
+  // null in decode.  total_q: all rows.
+  const int32_t* cu_seqlens_q;
+  int32_t total_q;
 };
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);
@@ -90,8 +95,12 @@ bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);
 // and the piece combine.
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
 int32_t decode_stream_resident_waves(int32_t cu_count, int32_t dtype);
-size_t decode_stream_workspace(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t resident_waves,
+// Workspace of a stream-split call whose pieces hold `columns` columns (the head
+// group in decode, kStreamMtColumns in multi-token decode).
+size_t decode_stream_workspace(int32_t batch, int32_t columns, int32_t num_kv_heads, int32_t resident_waves,
                                size_t* ws_o_offset, size_t* ws_ml_offset);
+// Multi-token decode through the stream split: (row, head) columns per KV head.
+constexpr int32_t kStreamMtColumns = 32;
 hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream);
 
 // Second pass of split-K decode: merges the partitions of each (sequence, head).

@@ -132,20 +132,46 @@ def test_stream_workspace_layout(lib):
 
 
 def test_prefill_workspace_of_the_key_split(lib):
-    """A multi-token decode (4 rows per sequence, G = 2: one 128-column workgroup per
-    sequence and KV head, 8 in all) over up to 8192 keys is split into 4 partitions of 2048
-    keys: partials for total_q x H rows x 4 (head_dim floats, 256-byte aligned, then (m, l)
-    pairs).  A grid that fills the GPU (the chunked prefill shapes) takes no workspace."""
+    """A few-row prefill (20 rows per sequence, G = 2: 40 columns per KV head, more than the
+    stream split's 32, so one 128-column workgroup per sequence and KV head, 8 in all) over
+    up to 8192 keys is split into 4 partitions of 2048 keys: partials for total_q x H rows x 4
+    (head_dim floats, 256-byte aligned, then (m, l) pairs).  A grid that fills the GPU (the
+    chunked prefill shapes) takes no workspace."""
     c = _cache()  # bf16, H_kv = 4, head_dim 128, block_size 128
     p = _params(batch=2, num_q_heads=8, max_blocks_per_seq=64)
-    rows = 8 * 8 * 4
-    need = lib.paged_attn_prefill_workspace(ctypes.byref(p), ctypes.byref(c), 8)
+    rows = 40 * 8 * 4
+    need = lib.paged_attn_prefill_workspace(ctypes.byref(p), ctypes.byref(c), 40)
     assert need == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
-    rc = lib.paged_attn_prefill(FAKE, None, ctypes.byref(c), FAKE, FAKE, FAKE, 8, 4, ctypes.byref(p), FAKE,
+    rc = lib.paged_attn_prefill(FAKE, None, ctypes.byref(c), FAKE, FAKE, FAKE, 40, 20, ctypes.byref(p), FAKE,
                                 None, 0, None)
     assert rc == 3 and "workspace" in lib.pkv_last_error().decode()
     big = _params(batch=8, num_q_heads=32, max_blocks_per_seq=36)
     assert lib.paged_attn_prefill_workspace(ctypes.byref(big), ctypes.byref(_cache(num_kv_heads=8)), 4096) == 0
+
+
+def test_prefill_workspace_of_the_stream_split(lib):
+    """Multi-token decode (4 rows per sequence, G = 2: 8 columns per KV head) may run on the
+    decode kernel's stream split, whose pieces hold 32 columns: the column prefix (B + 1 int32,
+    256-byte aligned), then pieces x 32 partial rows of head_dim floats (256-byte aligned) and
+    their (m, l) pairs, pieces = resident waves + B x H_kv.  The query, which sees total_q and
+    not max_q_len, answers with the larger of that and the prefill kernel's key split, so either
+    path the call then takes fits."""
+    c = _cache()  # bf16, H_kv = 4, head_dim 128
+    p = _params(batch=2, num_q_heads=8, max_blocks_per_seq=64)
+    need = lib.paged_attn_prefill_workspace(ctypes.byref(p), ctypes.byref(c), 8)
+    resident = 256 * 4  # CUs x 4 waves, the size query's figure without a GPU
+    pieces = resident + 2 * 4
+    stream = 256 + (pieces * 32 * 128 * 4 + 255) // 256 * 256 + pieces * 32 * 8
+    split_rows = 8 * 8 * 4
+    split = (split_rows * 128 * 4 + 255) // 256 * 256 + split_rows * 8
+    assert need == max(stream, split)
+    # 64-wide heads never take the stream split
+    c64 = _cache(head_dim=64)
+    assert lib.paged_attn_prefill_workspace(ctypes.byref(p), ctypes.byref(c64), 8) == \
+        (split_rows * 64 * 4 + 255) // 256 * 256 + split_rows * 8
+    rc = lib.paged_attn_prefill(FAKE, None, ctypes.byref(c), FAKE, FAKE, FAKE, 8, 4, ctypes.byref(p), FAKE,
+                                FAKE, stream - 1, None)
+    assert rc == 3 and "workspace" in lib.pkv_last_error().decode()
 
 
 @pytest.mark.parametrize("total_q,max_q_len,needle", [

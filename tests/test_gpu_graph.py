@@ -34,8 +34,10 @@ CASES = {
                                                 len_range=(1, 1200), rope_dim=64, scale=576 ** -0.5),
     "chunked prefill": lambda: workloads.prefill_case(9, 3, 16, 4, 128, "bf16", cached=[100, 0, 700],
                                                       new=[60, 33, 128], block_size=64),
-    "multi-token decode (key split + combine)": lambda: workloads.prefill_case(
+    "multi-token decode (stream split + combine)": lambda: workloads.prefill_case(
         10, 3, 16, 4, 128, "bf16", cached=[5000, 100, 3000], new=[4, 2, 3], block_size=128, null_block=True),
+    "few-row prefill (key split + combine)": lambda: workloads.prefill_case(
+        11, 3, 16, 4, 128, "bf16", cached=[5000, 100, 3000], new=[12, 9, 10], block_size=128, null_block=True),
 }
 
 

@@ -58,14 +58,16 @@ def test_prefill_matches_oracle(orc, shape):
     assert_rows_close(out, ref, BF16_TOL)
 
 
-# Multi-token decode shapes: so few (sequence, KV head, column tile) workgroups that the
-# keys are split into partitions of 2048 and the partials merged by the combine --
-# partitions past a short sequence or before its window are empty.
+# A few rows per sequence, but more (row, head) columns per KV head than the stream
+# split's two tiles hold (or 64-wide heads): so few (sequence, KV head, column tile)
+# workgroups that the prefill kernel's keys are split into partitions of 2048 and the
+# partials merged by the combine -- partitions past a short sequence or before its
+# window are empty.
 SPLIT_MATRIX = [
     # B, H, Hkv, D, bs, cached, new, window
-    (3, 16, 4, 128, 128, [5000, 100, 9000], [4, 2, 3], 0),
+    (3, 16, 4, 128, 128, [5000, 100, 9000], [12, 9, 10], 0),
     (2, 8, 2, 64, 32, [6000, 3000], [4, 1], 1000),
-    (4, 32, 8, 128, 64, [2047, 2048, 4095, 4100], [1, 2, 3, 4], 0),  # rows on partition edges
+    (4, 32, 8, 128, 64, [2047, 2048, 4095, 4100], [9, 10, 11, 12], 0),  # rows on partition edges
     (1, 16, 2, 128, 128, [20000], [40], 0),     # 320 columns: several column tiles per partition
     (1, 16, 2, 64, 64, [9000], [100], 3000),    # 800 columns under a window
 ]
@@ -86,6 +88,48 @@ def test_prefill_key_split_matches_oracle(orc, shape):
     np.testing.assert_array_equal(host(slots), slots_ref)
     assert_rows_close(out, ref, BF16_TOL)
     out32 = d.attend(out_dtype=torch.float32)
+    assert_rows_close(out32, ref, ACC_TOL)
+
+
+# Multi-token decode through the decode kernel's stream split: bf16, 128-wide heads and
+# at most 32 (row, head) columns per KV head -- one or two column tiles, ragged row
+# counts (an empty one included), windows, 16-token blocks, a batch past the in-LDS
+# column prefix.
+MT_MATRIX = [
+    # B, H, Hkv, bs, cached, new, window
+    (3, 16, 4, 128, [5000, 100, 9000], [4, 2, 3], 0),
+    (4, 32, 8, 64, [2047, 2048, 4095, 4100], [1, 2, 3, 4], 0),
+    (4, 64, 8, 128, [3000, 100, 7000, 33], [4, 4, 4, 4], 0),    # 70B heads: two column tiles
+    (3, 64, 8, 16, [3000, 5, 900], [4, 2, 3], 500),             # window over 16-token blocks
+    (2, 32, 2, 32, [700, 1500], [2, 1], 0),                      # 16 heads per KV head
+    (2, 4, 4, 128, [300, 1000], [32, 20], 0),                    # MHA, 32 rows
+    (3, 16, 8, 64, [0, 500, 17], [3, 0, 4], 7),                  # a sequence without rows, a tiny window
+    (2100, 8, 4, 16, (0, 40), (1, 2), 0),                        # batch past the in-LDS prefix
+]
+
+
+@pytest.mark.parametrize("shape", MT_MATRIX, ids=[f"mt{i}" for i in range(len(MT_MATRIX))])
+def test_multi_token_decode_stream_matches_oracle(orc, shape):
+    import paged_kv_cache_80_amd as pkv
+
+    B, H, Hkv, bs, cached, new, w = shape
+    if isinstance(cached, tuple):  # ranges: a seeded draw per sequence
+        rng = np.random.default_rng(B)
+        cached = rng.integers(cached[0], cached[1] + 1, size=B)
+        new = rng.integers(new[0], new[1] + 1, size=B)
+    case = workloads.prefill_case(int(np.sum(cached)) + w + 2, B, H, Hkv, 128, "bf16", cached=cached, new=new,
+                                  block_size=bs, window=w, null_block=True)
+    d = DeviceCase(case)
+    max_q = int(np.max(new))
+    assert max_q * (H // Hkv) <= 32, "these shapes take the stream split"
+    need = pkv.paged_attn_prefill_workspace(d.cache, B, H, case.max_blocks, case.q.shape[0], case.scale, w)
+    assert need > 0
+    ref, c_ref, slots_ref = oracle_run(orc, case)
+    out, slots = d.run()
+    np.testing.assert_array_equal(host(slots), slots_ref)
+    assert_rows_close(out, ref, BF16_TOL)
+    out32 = d.attend(out_dtype=torch.float32)
+    torch.cuda.synchronize()
     assert_rows_close(out32, ref, ACC_TOL)
 
 
