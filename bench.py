@@ -3,8 +3,8 @@
 
 One step = one pass of the whole path over one batch of synthetic input, all
 on the GPU through the C ABI:
-    pkv_resolve_slots (new tokens' slots through the block table)
-    -> kv_cache_write (scatter the new K/V rows into the paged cache)
+    kv_cache_write_at (the new tokens' slots resolved through the block table
+        and their K/V rows scattered into the paged cache, one launch)
     -> paged_attn_decode (split-K decode + combine) / paged_attn_prefill.
 Inputs are resident in HBM before the timed region.  Prints ONE JSON line.
 
@@ -124,11 +124,12 @@ def algorithmic_bytes(case):
     T = case.new_pos.size
     resolve = T * 16  # batch index, position, table entry, slot
     row = case.Hkv * case.D * eb
+    # the write resolves its slots itself (kv_cache_write_at): rows in, rows out
     if case.int8:  # bf16 rows in; codes and one float32 scale per (token, head) out
         stored = case.Hkv * (case.D + 4)
-        write = T * (4 + 2 * (row + stored))
+        write = T * 2 * (row + stored)
     else:
-        write = T * (4 + 2 * row * (1 if case.is_mla else 2) + (2 * case.Hkv * case.rope_dim * eb))
+        write = T * (2 * row * (1 if case.is_mla else 2) + (2 * case.Hkv * case.rope_dim * eb))
     if case.kind == "decode":
         lo = np.maximum(0, L - case.window) if case.window else np.zeros_like(L)
         keys = L - lo
@@ -457,10 +458,13 @@ MAP_WORKLOADS = ("tiny_f32_decode", "gqa_decode_70b", "gqa_decode_70b_window4096
 
 
 def read_ceiling(torch):
-    """The read bandwidth a plain streaming kernel reaches on this GPU in the same run: 1 GiB
-    read once by libpkv_probe.so (contiguous shares, 16-byte loads, sixteen in flight per
-    lane, 2 workgroups per CU), timed with HIP events on the stream it runs on.  The attainable reference for the
-    HBM-bound calls beside the 8 TB/s datasheet figure."""
+    """The read bandwidth plain streaming kernels reach on this GPU in the same run: 2 GiB
+    (the size of the llama2-7B decode's cache, so that ramp-up weighs the same) read once by
+    each kernel of libpkv_probe.so -- 16-byte loads into registers
+    (contiguous shares, sixteen in flight per lane, 2 workgroups per CU), and
+    global_load_lds DMA into LDS the way the decode kernels stream (four waves per CU,
+    16 KiB per step) -- timed with HIP events on the stream they run on.  The faster is the
+    attainable reference for the HBM-bound calls beside the 8 TB/s datasheet figure."""
     import ctypes
 
     path = os.path.join(ROOT, "paged_kv_cache_80_amd", "libpkv_probe.so")
@@ -472,31 +476,40 @@ def read_ceiling(torch):
     lib.pkv_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p]
     lib.pkv_probe_stream_read.restype = ctypes.c_int
-    n = 1 << 30
-    wgs = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    lib.pkv_probe_stream_read_lds.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p]
+    lib.pkv_probe_stream_read_lds.restype = ctypes.c_int
+    n = 2 << 30
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
-    sink = torch.empty(int(lib.pkv_probe_sink_words(wgs)), dtype=torch.int32, device="cuda")
+    sink = torch.empty(int(lib.pkv_probe_sink_words(2 * cus)), dtype=torch.int32, device="cuda")
     st = torch.cuda.current_stream()
 
-    def launch():
-        if lib.pkv_probe_stream_read(buf.data_ptr(), n, wgs, sink.data_ptr(), st.cuda_stream) != 0:
-            raise RuntimeError("read probe launch failed")
+    def regs():
+        return lib.pkv_probe_stream_read(buf.data_ptr(), n, 2 * cus, sink.data_ptr(), st.cuda_stream)
 
-    for _ in range(3):
-        launch()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    e0.record(st)
-    for _ in range(reps):
-        launch()
-    e1.record(st)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    def dma():
+        return lib.pkv_probe_stream_read_lds(buf.data_ptr(), n, cus, st.cuda_stream)
+
+    out = {}
+    for name, launch in (("registers", regs), ("lds_dma", dma)):
+        for _ in range(3):
+            if launch() != 0:
+                raise RuntimeError(f"read probe ({name}) launch failed")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(st)
+        for _ in range(reps):
+            launch()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"GBps": round(n / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4)}
     del buf, sink
     torch.cuda.empty_cache()
-    return {"GBps": round(n / (ms * 1e-3) / 1e9, 1), "ms": round(ms, 4), "bytes": n,
-            "what": "read-only streaming kernel over 1 GiB (libpkv_probe.so)"}
+    best = max(v["GBps"] for v in out.values())
+    return {"GBps": best, "bytes": n, **out,
+            "what": "read-only streaming kernels over 2 GiB (libpkv_probe.so); GBps is the faster"}
 
 
 def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass):
@@ -540,8 +553,7 @@ def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass):
 
     def step(i, e0=None, e1=None):
         c = caches[i % len(caches)]
-        pkv.pkv_resolve_slots(bt, case.block_size, bidx, pos, slots_out=slots)
-        pkv.kv_cache_write(slots, new_k, new_v, c, k_rope=new_kr)
+        pkv.kv_cache_write_at(bt, bidx, pos, new_k, new_v, c, k_rope=new_kr, slots_out=slots)
         if e0 is not None:
             e0.record()
         attend(c)

@@ -141,6 +141,21 @@ pkv_status kv_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const
                           const void* v, const void* k_rope, const pkv_paged_cache* cache,
                           void* stream);
 
+/* Index resolution and cache write in one launch: row t goes to the slot of
+ * (batch_idx[t], pos[t]), resolved through block_table exactly as
+ * pkv_resolve_slots does it ("KVCache optimisation skill", section 3.1), and is
+ * written exactly as kv_cache_write writes it (the guide's mode-2 scatter;
+ * quantized into a PKV_INT8 cache).  A negative pos skips the row.  When slots_out
+ * is not NULL it receives the resolved slots ([num_tokens], -1 for skipped rows),
+ * the slot_mapping kv_cache_write would have taken.
+ *   block_table : [batch, max_blocks_per_seq]; batch_idx, pos: [num_tokens]
+ *   k, v, k_rope: as for kv_cache_write.  The resolved slots must be distinct.
+ * Same errors as kv_cache_write, plus NULL index arrays or max_blocks_per_seq <= 0;
+ * the same int32 range rule for block ids as pkv_resolve_slots. */
+pkv_status kv_cache_write_at(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* batch_idx,
+                             const int32_t* pos, int32_t num_tokens, const void* k, const void* v,
+                             const void* k_rope, const pkv_paged_cache* cache, int32_t* slots_out, void* stream);
+
 typedef enum {
   PKV_ROPE_HALF = 0,       /* element i pairs with i + rope_dim/2 (the first half with the second) */
   PKV_ROPE_INTERLEAVED = 1 /* elements 2k and 2k+1 form a pair                                  */

@@ -34,7 +34,8 @@ STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED", 3: "P
           4: "PKV_ERR_HIP"}
 
 # Every symbol include/pkv.h declares.
-EXPORTS = ("pkv_resolve_slots", "paged_resolve_slots", "kv_cache_write", "kv_rmsnorm_rope_cache", "paged_attn_decode_workspace",
+EXPORTS = ("pkv_resolve_slots", "paged_resolve_slots", "kv_cache_write", "kv_cache_write_at", "kv_rmsnorm_rope_cache",
+           "paged_attn_decode_workspace",
            "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_noalloc_capacity",
            "paged_attn_prefill_workspace", "paged_attn_prefill", "pkv_last_error", "pkv_version")
 
@@ -96,6 +97,7 @@ def load(path: str = LIB_PATH):
     lib.pkv_resolve_slots.argtypes = [P, i32, i32, i32, P, P, i32, P, P]
     lib.paged_resolve_slots.argtypes = [P, i32, i32, P, P, i32, P, P]
     lib.kv_cache_write.argtypes = [P, i32, P, P, P, pc, P]
+    lib.kv_cache_write_at.argtypes = [P, i32, P, P, i32, P, P, P, pc, P, P]
     lib.kv_rmsnorm_rope_cache.argtypes = [P, P, P, P, P, i32, ctypes.c_float, i32, pc, P, P, P]
     lib.paged_attn_decode_workspace.argtypes = [pp, pc]
     lib.paged_attn_decode_workspace.restype = sz
@@ -106,7 +108,8 @@ def load(path: str = LIB_PATH):
     lib.paged_attn_prefill_workspace.argtypes = [pp, pc, i32]
     lib.paged_attn_prefill_workspace.restype = sz
     lib.paged_attn_prefill.argtypes = [P, P, pc, P, P, P, i32, i32, pp, P, P, sz, P]
-    for f in (lib.pkv_resolve_slots, lib.paged_resolve_slots, lib.kv_cache_write, lib.kv_rmsnorm_rope_cache, lib.paged_attn_decode,
+    for f in (lib.pkv_resolve_slots, lib.paged_resolve_slots, lib.kv_cache_write, lib.kv_cache_write_at,
+              lib.kv_rmsnorm_rope_cache, lib.paged_attn_decode,
               lib.paged_attn_decode_noalloc, lib.paged_attn_prefill):
         f.restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
@@ -252,6 +255,34 @@ def kv_cache_write(slot_mapping: torch.Tensor, k: torch.Tensor, v: Optional[torc
         _run_check(checks.check_slots, slot_mapping, d.num_blocks * d.block_size)
     _check(load().kv_cache_write(_ptr(_i32(slot_mapping)), slot_mapping.numel(), _ptr(k), _ptr(v),
                                  _ptr(k_rope), ctypes.byref(d), _stream(stream)))
+
+
+def kv_cache_write_at(block_table: torch.Tensor, batch_idx: torch.Tensor, pos: torch.Tensor, k: torch.Tensor,
+                      v: Optional[torch.Tensor], cache: PagedKVCache, k_rope: Optional[torch.Tensor] = None,
+                      slots_out: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """Resolve (batch_idx[t], pos[t]) through block_table and write row t there, in one launch
+    (pos < 0 skips the row).  Returns slots_out, which receives the resolved slots when given."""
+    bt = _i32(block_table)
+    n = batch_idx.numel()
+    if bt.dim() != 2:
+        raise ValueError("block_table must be [batch, max_blocks_per_seq]")
+    _expect(pos, (n,), "pos")
+    _expect(slots_out, (n,), "slots_out")
+    _, bs, hkv, hd = cache.k_cache.shape
+    _expect(k, (n, hkv, hd), "k")
+    _expect(v, (n, hkv, hd), "v")
+    if k_rope is not None:
+        _expect(k_rope, (n, hkv, cache.k_rope_cache.shape[3]), "k_rope")
+    _check_elems(cache, k, v, k_rope)
+    d = cache.desc()
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_write_at, bt, bs, batch_idx, pos, d.num_blocks)
+    if slots_out is not None:
+        _i32(slots_out)
+    _check(load().kv_cache_write_at(_ptr(bt), bt.shape[1], _ptr(_i32(batch_idx)), _ptr(_i32(pos)), n, _ptr(k), _ptr(v),
+                                    _ptr(k_rope), ctypes.byref(d), _ptr(slots_out), _stream(stream)))
+    return slots_out
 
 
 def kv_rmsnorm_rope_cache(latent: torch.Tensor, gamma: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,

@@ -82,6 +82,19 @@ def check_resolve(block_table, block_size: int, batch_idx, pos, num_blocks: int 
               f"not one of {limit}")
 
 
+def check_write_at(block_table, block_size: int, batch_idx, pos, num_blocks: int) -> None:
+    """kv_cache_write_at: every (batch_idx, pos >= 0) resolves through a pool block id, and the
+    resolved slots are distinct."""
+    check_resolve(block_table, block_size, batch_idx, pos, num_blocks)
+    bt = _host(block_table).astype(np.int64)
+    b = _host(batch_idx).astype(np.int64).ravel()
+    p = _host(pos).astype(np.int64).ravel()
+    live = p >= 0
+    slots = np.full(p.shape, -1, dtype=np.int64)
+    slots[live] = bt[b[live], p[live] // block_size] * block_size + p[live] % block_size
+    check_slots(slots, num_blocks * block_size)
+
+
 def check_decode(block_table, seq_lens, block_size: int, num_blocks: int, window: int = 0) -> None:
     """paged_attn_decode: 0 <= seq_lens[b] <= table width, and the blocks of the visible keys
     [max(0, L - W), L) hold valid ids."""

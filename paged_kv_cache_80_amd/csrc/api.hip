@@ -279,6 +279,55 @@ pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache*
                        const int32_t* seq_lens, const pkv_attn_params* params, void* out, void* workspace,
                        size_t workspace_bytes, void* stream, bool static_scratch);
 
+pkv_status write_impl(const pkv::SlotSource& slots, int32_t num_tokens, const void* k, const void* v,
+                      const void* k_rope, const pkv_paged_cache* cache, void* stream) {
+  pkv_status s = check_cache(cache);
+  if (s) return s;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %d must be >= 0", num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!k) return fail(PKV_ERR_INVALID_ARG, "k must not be NULL");
+  const bool shared_kv = cache->v_cache == cache->k_cache;
+  if (shared_kv && v) return fail(PKV_ERR_INVALID_ARG, "v must be NULL when v_cache aliases k_cache");
+  if (!shared_kv && !v) return fail(PKV_ERR_INVALID_ARG, "v must not be NULL");
+  if ((cache->rope_dim > 0) != (k_rope != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_rope must be given exactly when the cache has a rope part");
+  if (!aligned16(k) || (v && !aligned16(v)) || (k_rope && !aligned16(k_rope)))
+    return fail(PKV_ERR_INVALID_ARG, "k / v / k_rope must be 16-byte aligned");
+  if (is_int8(cache)) {
+    pkv::Int8WriteArgs w{};
+    w.k = k;
+    w.v = v;
+    w.k_cache = cache->k_cache;
+    w.v_cache = cache->v_cache;
+    w.k_scale = static_cast<float*>(cache->k_scale);
+    w.v_scale = static_cast<float*>(cache->v_scale);
+    w.num_tokens = num_tokens;
+    w.num_kv_heads = cache->num_kv_heads;
+    w.block_size_log2 = log2i(cache->block_size);
+    return from_hip(pkv::launch_cache_write_int8(slots, w, static_cast<hipStream_t>(stream)), "cache write launch");
+  }
+  pkv::WriteRows rows{};
+  const int32_t eb = elem_bytes(cache->dtype);
+  rows.src[0] = k;
+  rows.dst[0] = cache->k_cache;
+  rows.row_bytes[0] = cache->num_kv_heads * cache->head_dim * eb;
+  rows.count = 1;
+  if (!shared_kv) {
+    rows.src[1] = v;
+    rows.dst[1] = cache->v_cache;
+    rows.row_bytes[1] = rows.row_bytes[0];
+    rows.count = 2;
+  }
+  if (cache->rope_dim > 0) {
+    rows.src[rows.count] = k_rope;
+    rows.dst[rows.count] = cache->k_rope_cache;
+    rows.row_bytes[rows.count] = cache->num_kv_heads * cache->rope_dim * eb;
+    rows.count++;
+  }
+  return from_hip(pkv::launch_cache_write(slots, num_tokens, rows, static_cast<hipStream_t>(stream)),
+                  "cache write launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -315,52 +364,28 @@ pkv_status paged_resolve_slots(const int32_t* block_table, int32_t max_blocks_pe
 
 pkv_status kv_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const void* k, const void* v,
                           const void* k_rope, const pkv_paged_cache* cache, void* stream) {
-  pkv_status s = check_cache(cache);
-  if (s) return s;
-  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %d must be >= 0", num_tokens);
-  if (num_tokens == 0) return ok();
-  if (!slot_mapping || !k) return fail(PKV_ERR_INVALID_ARG, "slot_mapping and k must not be NULL");
-  const bool shared_kv = cache->v_cache == cache->k_cache;
-  if (shared_kv && v) return fail(PKV_ERR_INVALID_ARG, "v must be NULL when v_cache aliases k_cache");
-  if (!shared_kv && !v) return fail(PKV_ERR_INVALID_ARG, "v must not be NULL");
-  if ((cache->rope_dim > 0) != (k_rope != nullptr))
-    return fail(PKV_ERR_INVALID_ARG, "k_rope must be given exactly when the cache has a rope part");
-  if (!aligned16(k) || (v && !aligned16(v)) || (k_rope && !aligned16(k_rope)))
-    return fail(PKV_ERR_INVALID_ARG, "k / v / k_rope must be 16-byte aligned");
-  if (is_int8(cache)) {
-    pkv::Int8WriteArgs w{};
-    w.k = k;
-    w.v = v;
-    w.k_cache = cache->k_cache;
-    w.v_cache = cache->v_cache;
-    w.k_scale = static_cast<float*>(cache->k_scale);
-    w.v_scale = static_cast<float*>(cache->v_scale);
-    w.num_tokens = num_tokens;
-    w.num_kv_heads = cache->num_kv_heads;
-    w.block_size_log2 = log2i(cache->block_size);
-    return from_hip(pkv::launch_cache_write_int8(slot_mapping, w, static_cast<hipStream_t>(stream)),
-                    "kv_cache_write launch");
-  }
-  pkv::WriteRows rows{};
-  const int32_t eb = elem_bytes(cache->dtype);
-  rows.src[0] = k;
-  rows.dst[0] = cache->k_cache;
-  rows.row_bytes[0] = cache->num_kv_heads * cache->head_dim * eb;
-  rows.count = 1;
-  if (!shared_kv) {
-    rows.src[1] = v;
-    rows.dst[1] = cache->v_cache;
-    rows.row_bytes[1] = rows.row_bytes[0];
-    rows.count = 2;
-  }
-  if (cache->rope_dim > 0) {
-    rows.src[rows.count] = k_rope;
-    rows.dst[rows.count] = cache->k_rope_cache;
-    rows.row_bytes[rows.count] = cache->num_kv_heads * cache->rope_dim * eb;
-    rows.count++;
-  }
-  return from_hip(pkv::launch_cache_write(slot_mapping, num_tokens, rows, static_cast<hipStream_t>(stream)),
-                  "kv_cache_write launch");
+  if (num_tokens > 0 && !slot_mapping) return fail(PKV_ERR_INVALID_ARG, "slot_mapping must not be NULL");
+  pkv::SlotSource src{};
+  src.slot_mapping = slot_mapping;
+  return write_impl(src, num_tokens, k, v, k_rope, cache, stream);
+}
+
+pkv_status kv_cache_write_at(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* batch_idx,
+                             const int32_t* pos, int32_t num_tokens, const void* k, const void* v, const void* k_rope,
+                             const pkv_paged_cache* cache, int32_t* slots_out, void* stream) {
+  pkv_status st = check_cache(cache);
+  if (st) return st;
+  if (num_tokens > 0 && (!block_table || !batch_idx || !pos))
+    return fail(PKV_ERR_INVALID_ARG, "block_table, batch_idx and pos must not be NULL");
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0");
+  pkv::SlotSource src{};
+  src.block_table = block_table;
+  src.batch_idx = batch_idx;
+  src.pos = pos;
+  src.slots_out = slots_out;
+  src.max_blocks_per_seq = max_blocks_per_seq;
+  src.block_size_log2 = log2i(cache->block_size);
+  return write_impl(src, num_tokens, k, v, k_rope, cache, stream);
 }
 
 pkv_status kv_rmsnorm_rope_cache(const void* latent, const void* gamma, const void* cos, const void* sin,

@@ -21,7 +21,18 @@ struct WriteRows {
   int32_t row_bytes[3];
   int32_t count;
 };
-hipError_t launch_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const WriteRows& rows,
+// Where a write's rows go: slot_mapping[t], or -- the fused form -- the slot of
+// (batch_idx[t], pos[t]) resolved through block_table, stored to slots_out too
+// when that is given (a negative pos gives -1: the row is skipped).
+struct SlotSource {
+  const int32_t* slot_mapping;  // non-null: the slots are given
+  const int32_t* block_table;
+  const int32_t* batch_idx;
+  const int32_t* pos;
+  int32_t* slots_out;
+  int32_t max_blocks_per_seq, block_size_log2;
+};
+hipError_t launch_cache_write(const SlotSource& slots, int32_t num_tokens, const WriteRows& rows,
                               hipStream_t stream);
 
 // Quantizing cache write into an int8 cache (write.hip): every (token, head) row
@@ -35,7 +46,7 @@ struct Int8WriteArgs {
   float* v_scale;
   int32_t num_tokens, num_kv_heads, block_size_log2;
 };
-hipError_t launch_cache_write_int8(const int32_t* slot_mapping, const Int8WriteArgs& a, hipStream_t stream);
+hipError_t launch_cache_write_int8(const SlotSource& slots, const Int8WriteArgs& a, hipStream_t stream);
 
 // Fused RMSNorm + RoPE + cache write of the MLA latent (latent_write.hip).
 // Latent width 512, rotary width 64, one latent head; every array in one dtype.

@@ -28,13 +28,23 @@ __global__ __launch_bounds__(256) void resolve_slots_kernel(const int32_t* __res
   slots[i] = (blk << bs_log2) + (p & ((1 << bs_log2) - 1));
 }
 
+// Slot of row t: given, or resolved from (batch_idx[t], pos[t]) as above.
+__device__ __forceinline__ int32_t slot_of(const SlotSource& s, int64_t t) {
+  if (s.slot_mapping) return s.slot_mapping[t];
+  const int32_t p = s.pos[t];
+  if (p < 0) return -1;
+  const int32_t blk = s.block_table[(int64_t)s.batch_idx[t] * s.max_blocks_per_seq + (p >> s.block_size_log2)];
+  return (blk << s.block_size_log2) + (p & ((1 << s.block_size_log2) - 1));
+}
+
 // One workgroup per token.  The token's K, V and rope rows are treated as one
 // list of 16-byte chunks; consecutive threads copy consecutive chunks, so every
-// wave reads and writes whole 1 KiB runs of each row.
-__global__ __launch_bounds__(256) void cache_write_kernel(const int32_t* __restrict__ slot_mapping,
-                                                          WriteRows rows) {
+// wave reads and writes whole 1 KiB runs of each row.  With the slots resolved
+// here (kv_cache_write_at), the index resolution and the write are one launch.
+__global__ __launch_bounds__(256) void cache_write_kernel(SlotSource slots, WriteRows rows) {
   const int32_t t = blockIdx.x;
-  const int32_t slot = slot_mapping[t];
+  const int32_t slot = __builtin_amdgcn_readfirstlane(slot_of(slots, t));
+  if (slots.slots_out && threadIdx.x == 0) slots.slots_out[t] = slot;
   if (slot < 0) return;
   for (int r = 0; r < rows.count; ++r) {
     const int32_t chunks = rows.row_bytes[r] >> 4;
@@ -50,8 +60,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const int32_t* __restr
 // IEEE float32, ties of rint to even), which leaves every code in [-127, 127];
 // an all-zero row gets s = 0 and zero codes.  Groups take the K rows of all
 // tokens first, then the V rows.
-__global__ __launch_bounds__(256) void cache_write_int8_kernel(const int32_t* __restrict__ slot_mapping,
-                                                               Int8WriteArgs a) {
+__global__ __launch_bounds__(256) void cache_write_int8_kernel(SlotSource slots, Int8WriteArgs a) {
   constexpr int kD = 128;
   const int64_t grp = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4);
   const int l = threadIdx.x & 15;
@@ -61,7 +70,8 @@ __global__ __launch_bounds__(256) void cache_write_int8_kernel(const int32_t* __
   const int64_t r = is_v ? grp - rows : grp;
   const int64_t t = r / a.num_kv_heads;
   const int h = (int)(r - t * a.num_kv_heads);
-  const int32_t slot = slot_mapping[t];
+  const int32_t slot = slot_of(slots, t);
+  if (slots.slots_out && !is_v && h == 0 && l == 0) slots.slots_out[t] = slot;
   if (slot < 0) return;
   const uint4 w = ld16(static_cast<const uint16_t*>(is_v ? a.v : a.k) + r * kD + 8 * l);
   const uint32_t u[4] = {w.x, w.y, w.z, w.w};
@@ -104,17 +114,17 @@ hipError_t launch_resolve_slots(const int32_t* block_table, int32_t batch, int32
   return hipGetLastError();
 }
 
-hipError_t launch_cache_write(const int32_t* slot_mapping, int32_t num_tokens, const WriteRows& rows,
+hipError_t launch_cache_write(const SlotSource& slots, int32_t num_tokens, const WriteRows& rows,
                               hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
-  cache_write_kernel<<<num_tokens, 256, 0, stream>>>(slot_mapping, rows);
+  cache_write_kernel<<<num_tokens, 256, 0, stream>>>(slots, rows);
   return hipGetLastError();
 }
 
-hipError_t launch_cache_write_int8(const int32_t* slot_mapping, const Int8WriteArgs& a, hipStream_t stream) {
+hipError_t launch_cache_write_int8(const SlotSource& slots, const Int8WriteArgs& a, hipStream_t stream) {
   const int64_t groups = 2 * (int64_t)a.num_tokens * a.num_kv_heads;
   if (groups == 0) return hipSuccess;
-  cache_write_int8_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, stream>>>(slot_mapping, a);
+  cache_write_int8_kernel<<<(unsigned)((groups + 15) / 16), 256, 0, stream>>>(slots, a);
   return hipGetLastError();
 }
 

@@ -450,3 +450,41 @@ def test_unused_table_entries_prefill(orc, rope):
     assert (poisoned.block_table == -1).any()
     out32, _ = DeviceCase(poisoned).run(out_dtype=torch.float32)
     assert_rows_close(out32, ref, ACC_TOL)
+
+
+# --------------------------------------------------------------------------- fused resolve + write
+
+WRITE_AT_CASES = [
+    # name, decode_case args (B, H, Hkv, D, dtype), block_size, rope, int8
+    ("bf16, 128-token blocks", (9, 16, 4, 128, "bf16"), 128, 0, False),
+    ("f32, 16-token blocks", (5, 8, 2, 64, "f32"), 16, 0, False),
+    ("MLA latent + rope", (6, 16, 1, 512, "bf16"), 32, 64, False),
+    ("int8, 16-token blocks", (7, 16, 4, 128, "bf16"), 16, 0, True),
+]
+
+
+@pytest.mark.parametrize("spec", WRITE_AT_CASES, ids=[x[0] for x in WRITE_AT_CASES])
+def test_write_at_equals_resolve_then_write(spec):
+    """kv_cache_write_at (slots resolved inside the write kernel) leaves the cache bit for bit
+    as pkv_resolve_slots followed by kv_cache_write does, skips rows with a negative position,
+    and returns the same slots."""
+    import paged_kv_cache_80_amd as pkv
+    name, (B, H, Hkv, D, dt), bs, rope, int8 = spec
+    case = workloads.decode_case(91 + B, B, H, Hkv, D, dt, block_size=bs, max_blocks=-(-700 // bs),
+                                 len_range=(1, 700), null_block=True, rope_dim=rope, int8=int8)
+    pos = case.new_pos.copy()
+    pos[1] = -1  # a skipped row
+    a, b = DeviceCase(case), DeviceCase(case)
+    dpos = dev(pos)
+    slots_ref = pkv.pkv_resolve_slots(a.block_table, bs, a.new_batch_idx, dpos)
+    pkv.kv_cache_write(slots_ref, a.new_k, a.new_v, a.cache, k_rope=a.new_k_rope)
+    slots = torch.full((case.B,), 7, dtype=torch.int32, device="cuda")
+    pkv.kv_cache_write_at(b.block_table, b.new_batch_idx, dpos, b.new_k, b.new_v, b.cache, k_rope=b.new_k_rope,
+                          slots_out=slots)
+    torch.cuda.synchronize()
+    assert host(slots).tolist() == host(slots_ref).tolist() and host(slots)[1] == -1
+    for x, y in ((a.cache.k_cache, b.cache.k_cache), (a.cache.v_cache, b.cache.v_cache),
+                 (a.cache.k_rope_cache, b.cache.k_rope_cache), (a.cache.k_scale, b.cache.k_scale),
+                 (a.cache.v_scale, b.cache.v_scale)):
+        if x is not None:
+            assert host(x).tobytes() == host(y).tobytes()

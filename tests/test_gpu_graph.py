@@ -64,8 +64,12 @@ def test_step_replays_in_a_graph(name):
     max_q = int(np.diff(case.cu_seqlens_q).max(initial=0)) if case.kind == "prefill" else 1
 
     def step():
-        pkv.pkv_resolve_slots(d.block_table, case.block_size, d.new_batch_idx, d.new_pos, slots_out=slots)
-        pkv.kv_cache_write(slots, d.new_k, d.new_v, d.cache, k_rope=d.new_k_rope)
+        if name.startswith("bf16"):  # index resolution fused into the write
+            pkv.kv_cache_write_at(d.block_table, d.new_batch_idx, d.new_pos, d.new_k, d.new_v, d.cache,
+                                  k_rope=d.new_k_rope, slots_out=slots)
+        else:
+            pkv.pkv_resolve_slots(d.block_table, case.block_size, d.new_batch_idx, d.new_pos, slots_out=slots)
+            pkv.kv_cache_write(slots, d.new_k, d.new_v, d.cache, k_rope=d.new_k_rope)
         if case.kind == "decode":
             pkv.paged_attn_decode(d.q, d.cache, d.block_table, d.seq_lens, case.scale, case.window,
                                   q_rope=d.q_rope, out=out, workspace=ws)

@@ -122,3 +122,12 @@ def test_resolve_checks():
     huge = np.array([[2**27]], dtype=np.int32)
     with pytest.raises(checks.IndexCheckError, match="block id"):
         checks.check_resolve(huge, 16, np.array([0]), np.array([0]))
+
+
+def test_write_at_checks():
+    bt = np.array([[2, 0], [1, 3]], dtype=np.int32)
+    checks.check_write_at(bt, 4, np.array([0, 1, 1, 0]), np.array([5, 0, -1, 1]), num_blocks=4)
+    with pytest.raises(checks.IndexCheckError, match="twice"):  # positions 1 and 5 both land in slot 5
+        checks.check_write_at(np.array([[1, 1]], dtype=np.int32), 4, np.array([0, 0]), np.array([1, 5]), num_blocks=2)
+    with pytest.raises(checks.IndexCheckError, match="block id"):
+        checks.check_write_at(bt, 4, np.array([1]), np.array([4]), num_blocks=3)
