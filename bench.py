@@ -161,7 +161,8 @@ PROFILED = {
     "gqa_decode_70b": ("decode_stream_gqa_decode_70b.md", _STREAM),
     "gqa_decode_70b_window4096": ("decode_stream_gqa_decode_70b_window4096.md", _STREAM),
     "chunked_prefill": ("prefill_mfma_chunked_prefill.md", [_CSRC + "prefill.hip"] + _COMMON),
-    "gqa_mtp_decode": ("prefill_mfma_gqa_mtp_decode.md", [_CSRC + "prefill.hip"] + _COMMON),
+    "gqa_mtp_decode": ("decode_stream_gqa_mtp_decode.md", _STREAM),
+    "tiny_f32_decode": ("decode_valu_tiny_f32_decode.md", [_CSRC + "decode.hip"] + _COMMON),
     "mla_decode": ("mla_decode_mla_decode.md", [_CSRC + "mla.hip", _CSRC + "decode.hip"] + _COMMON),
     "mla_mtp_decode": ("mla_decode_mla_mtp_decode.md", [_CSRC + "mla.hip"] + _COMMON),
     "mla_chunked_prefill": ("mla_decode_mla_chunked_prefill.md", [_CSRC + "mla.hip"] + _COMMON),
@@ -512,7 +513,7 @@ def read_ceiling(torch):
             "what": "read-only streaming kernels over 2 GiB (libpkv_probe.so); GBps is the faster"}
 
 
-def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass):
+def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass, graph=None):
     """Time `steps` steps (resolve -> write -> attention) of one workload after `warmup`
     untimed ones, on cold-cache copies; returns the result fields of the JSON line."""
     dev = lambda a: _dev(torch, a)  # noqa: E731
@@ -562,6 +563,7 @@ def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass):
 
     ms_step, ms_attn, med_attn = _timed(torch, step, steps, warmup)
     warm = _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), steps, warmup) if warm_pass else None
+    graph_ms = graph_step_ms(torch, step, steps) if (warm_pass if graph is None else graph) else None
 
     r_b, w_b, a_b, kv_b = algorithmic_bytes(case)
     flops = algorithmic_flops(case)
@@ -597,11 +599,43 @@ def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass):
         res["warm"] = {"ms_per_step": round(warm[0], 4), "attention_ms": round(warm[1], 4),
                        "attention_GBps": round(a_b / (warm[1] * 1e-3) / 1e9, 2),
                        "mfma_util": round(flops / (warm[1] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if graph_ms is not None:
+        res["graph"] = {"ms_per_step": round(graph_ms, 4), "GBps": round(step_bytes / (graph_ms * 1e-3) / 1e9, 2),
+                        "steps": steps, "what": "the same cold-cache steps captured once in a HIP graph and "
+                                                "replayed, with no host launch between kernels"}
     if a_b < LATENCY_BYTES:
         res["device_latency"] = backlogged_times(torch, lambda: attend(caches[0]), lambda: step(0))
     if cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(case, cpu_seconds)
     return res
+
+
+def graph_step_ms(torch, step, steps):
+    """ms per step of `steps` consecutive steps (the same rotation over cache copies) captured
+    once in a HIP graph and replayed between two events: the step as a serving loop that
+    captures its decode step runs it, without the host's launch gaps between kernels.  No
+    entry point allocates, synchronises or clears memory, so a step captures."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    g.replay()  # warm-up replay
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del g
+    return ms
 
 
 # Calls that move fewer bytes than this are latency-bound: the eager event pair around the
@@ -645,7 +679,8 @@ def backlogged_times(torch, attend_once, step_once, reps=50):
 def map_entry(res, ceiling):
     """The compact record of a workload in the line's "workloads" map."""
     e = {k: res[k] for k in ("config", "attention_ms", "attention_ms_median", "attention_GBps", "mfma_util",
-                             "tokens_per_s", "roofline", "cold_cache", "device_latency", "cpu_baseline") if k in res}
+                             "tokens_per_s", "roofline", "cold_cache", "graph", "device_latency", "cpu_baseline")
+         if k in res}
     e["ms_per_step"] = round(res["ms_per_step"], 4)
     e["step_GBps"] = round(res["value"], 2)
     if "device_latency" in res:  # latency-bound: a time, not a roofline fraction, is the figure
@@ -701,7 +736,7 @@ def main():
             c = workloads.WORKLOADS[other](args.seed)
             c.seed_label = args.seed
             r = measure(args, c, torch, pkv, args.map_steps, 3,
-                        0.0 if args.no_cpu_baseline else args.map_cpu_seconds, False)
+                        0.0 if args.no_cpu_baseline else args.map_cpu_seconds, False, graph=True)
             del c
             torch.cuda.empty_cache()
             wl[other] = map_entry(r, ceiling)

@@ -718,13 +718,22 @@ __global__ __launch_bounds__(kWaves * kWave) void stream_combine_kernel(DecodeAr
   const int g = h / G;
   int b = t, c = h % G;
   if constexpr (MT) {
+    // b = the last sequence with cu[b] <= t, found 64 samples at a time: the
+    // lanes read 64 evenly spaced entries of [lo, hi] at once and the range
+    // shrinks to the gap between the last sample <= t and the first one past it
+    // (a range of at most 64 entries is sampled whole, so one round trip ends it).
     const int32_t* cu = a.cu_seqlens_q;
-    int lo_b = 0, hi_b = a.batch - 1;  // the last b with cu[b] <= t
-    while (lo_b < hi_b) {
-      const int mid = (lo_b + hi_b + 1) >> 1;
-      if (cu[mid] <= t) lo_b = mid; else hi_b = mid - 1;
+    int lo = 0, hi = a.batch - 1;
+    while (hi > lo) {
+      const int64_t span = hi - lo + 1;
+      const bool le = cu[lo + (int)(span * lane / kWave)] <= t;
+      const uint64_t m = __ballot(le);  // a prefix of the lanes: cu never decreases
+      const int k_last = 63 - __builtin_clzll(m);  // lane 0 samples lo, where cu[lo] <= t
+      const int64_t next = ~m ? lo + span * __builtin_ctzll(~m) / kWave : hi + 1;
+      lo = lo + (int)(span * k_last / kWave);
+      hi = (int)next - 1;
     }
-    b = lo_b;
+    b = lo;
     c += (t - cu[b]) * G;
   }
   const int64_t cols = MT ? kStreamCols : G;  // columns of a piece
