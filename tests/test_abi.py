@@ -117,6 +117,25 @@ def test_workspace_size_formula(lib):
     assert lib.paged_attn_decode_workspace(ctypes.byref(p1), ctypes.byref(c)) == 0
 
 
+def test_small_vector_alu_decodes_take_short_partitions(lib):
+    """The partition length of the vector-ALU decode when the caller gives none: 512 keys,
+    shorter (down to 128) while B * H_kv workgroups per partition would leave CUs idle
+    (256 CUs assumed without a GPU).  The tiny fp32 decode (2 sequences x 4 KV heads, 4
+    blocks of 128) takes four 128-key partitions; 64 pairs take 128-key partitions as well
+    (64 x 4 workgroups); 512 pairs keep whole 512-key sequences (no workspace)."""
+    c = _cache(dtype=pkv.PKV_F32, num_kv_heads=4)
+
+    def ws(batch, heads):
+        return lib.paged_attn_decode_workspace(ctypes.byref(_params(batch=batch, num_q_heads=heads)),
+                                               ctypes.byref(c))
+
+    rows = 2 * 4 * 4
+    assert ws(2, 4) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
+    rows = 16 * 4 * 4
+    assert ws(16, 4) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
+    assert ws(128, 4) == 0
+
+
 def test_stream_workspace_layout(lib):
     """Stream split (bf16, head_dim 128): the tile prefix (B+1 int32, 256-byte aligned), then
     one (G x head_dim) partial and G (m, l) pairs per piece, pieces = resident waves + B*H_kv.
