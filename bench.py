@@ -513,9 +513,18 @@ def read_ceiling(torch):
             "what": "read-only streaming kernels over 2 GiB (libpkv_probe.so); GBps is the faster"}
 
 
+def fused_append(case) -> bool:
+    """Decode steps the library runs as one call (paged_attn_decode_append: the bf16
+    stream split writes each sequence's newest row inside the decode kernel)."""
+    return (case.kind == "decode" and case.dtype == "bf16" and not case.int8 and not case.is_mla
+            and case.D == 128 and case.G <= 16)
+
+
 def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass, graph=None):
-    """Time `steps` steps (resolve -> write -> attention) of one workload after `warmup`
-    untimed ones, on cold-cache copies; returns the result fields of the JSON line."""
+    """Time `steps` steps of one workload after `warmup` untimed ones, on cold-cache copies;
+    returns the result fields of the JSON line.  A step is the append fused into the decode
+    (one call) where the library fuses it, else the write (slots resolved in the writer)
+    and then the attention call."""
     dev = lambda a: _dev(torch, a)  # noqa: E731
     if case.int8:
         cache = int8_cache(torch, pkv, case)
@@ -552,12 +561,22 @@ def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass, graph
                                                                       cl(cache.k_rope_cache), cl(cache.k_scale),
                                                                       cl(cache.v_scale)), cache_bytes)
 
+    fused = fused_append(case)
+
+    def append_attend(c):
+        pkv.paged_attn_decode_append(q, new_k, new_v, c, bt, sl, case.scale, case.window, out=out,
+                                     split_tokens=args.split_tokens, workspace=ws)
+
     def step(i, e0=None, e1=None):
         c = caches[i % len(caches)]
-        pkv.kv_cache_write_at(bt, bidx, pos, new_k, new_v, c, k_rope=new_kr, slots_out=slots)
+        if not fused:
+            pkv.kv_cache_write_at(bt, bidx, pos, new_k, new_v, c, k_rope=new_kr, slots_out=slots)
         if e0 is not None:
             e0.record()
-        attend(c)
+        if fused:
+            append_attend(c)
+        else:
+            attend(c)
         if e1 is not None:
             e1.record()
 
@@ -568,10 +587,13 @@ def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass, graph
     r_b, w_b, a_b, kv_b = algorithmic_bytes(case)
     flops = algorithmic_flops(case)
     step_bytes = r_b + w_b + a_b
+    if fused:  # the timed call is the whole step: its bytes include the append
+        a_b = step_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     attn_gbs = a_b / (ms_attn * 1e-3) / 1e9
     attn_tflops = flops / (ms_attn * 1e-3) / 1e12
-    kernel = "paged_attn_decode" if case.kind == "decode" else "paged_attn_prefill"
+    kernel = ("paged_attn_decode_append" if fused else "paged_attn_decode") if case.kind == "decode" \
+        else "paged_attn_prefill"
     # The bound is the one the call's arithmetic intensity meets first: flops per
     # algorithmic byte against the ridge of 2.5 PFLOP/s over 8 TB/s (312.5 flop/B).
     if flops / a_b >= MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
@@ -604,7 +626,8 @@ def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass, graph
                         "steps": steps, "what": "the same cold-cache steps captured once in a HIP graph and "
                                                 "replayed, with no host launch between kernels"}
     if a_b < LATENCY_BYTES:
-        res["device_latency"] = backlogged_times(torch, lambda: attend(caches[0]), lambda: step(0))
+        res["device_latency"] = backlogged_times(torch, lambda: (append_attend if fused else attend)(caches[0]),
+                                                 lambda: step(0))
     if cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(case, cpu_seconds)
     return res

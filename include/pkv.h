@@ -208,6 +208,29 @@ pkv_status paged_attn_decode(const void* q, const void* q_rope, const pkv_paged_
                              const pkv_attn_params* params, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* A decode step with its cache append: for every sequence b with seq_lens[b] > 0,
+ * the row k_new[b] (and v_new[b], and for MLA k_rope_new[b]) is written to the
+ * cache at position seq_lens[b] - 1 -- the slot block_table[b][p / bs] * bs + p % bs
+ * of the "KVCache optimisation skill" page's address map, as kv_cache_write_at would
+ * -- and then the decode above runs over keys that include it, exactly as
+ * paged_attn_decode.  The skill page's decode data flow writes the step's token
+ * and then attends with seq_len + 1 keys; this is those two calls as one.
+ *   k_new, v_new : [batch, num_kv_heads, head_dim] in the cache's storage type
+ *                  (bf16 or fp32; bf16 rows for an int8 cache, quantized as
+ *                  kv_cache_write does); v_new NULL when v_cache aliases k_cache
+ *   k_rope_new   : [batch, 1, rope_dim] iff the cache has a rope part, else NULL
+ *   other arguments, workspace, results and errors: as paged_attn_decode
+ * On the bf16 stream-split path (bf16 cache, head_dim 128) it is one kernel: the
+ * wave that reads a sequence's newest key takes it from k_new / v_new and stores
+ * it at its slot.  Other caches write the rows first and then decode (two
+ * launches, the same results).  The rows' slots must not be read by another call
+ * running at the same time, and two sequences must not share the newest slot. */
+pkv_status paged_attn_decode_append(const void* q, const void* q_rope, const void* k_new, const void* v_new,
+                                    const void* k_rope_new, const pkv_paged_cache* cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const pkv_attn_params* params, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* For callers that cannot allocate -- code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc: paged_attn_decode with no workspace
  * argument.  Its scratch space (the partial outputs of the split) is a

@@ -36,7 +36,8 @@ STATUS = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_UNSUPPORTED", 3: "P
 # Every symbol include/pkv.h declares.
 EXPORTS = ("pkv_resolve_slots", "paged_resolve_slots", "kv_cache_write", "kv_cache_write_at", "kv_rmsnorm_rope_cache",
            "paged_attn_decode_workspace",
-           "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_noalloc_capacity",
+           "paged_attn_decode", "paged_attn_decode_append", "paged_attn_decode_noalloc",
+           "paged_attn_decode_noalloc_capacity",
            "paged_attn_prefill_workspace", "paged_attn_prefill", "pkv_last_error", "pkv_version")
 
 
@@ -102,6 +103,7 @@ def load(path: str = LIB_PATH):
     lib.paged_attn_decode_workspace.argtypes = [pp, pc]
     lib.paged_attn_decode_workspace.restype = sz
     lib.paged_attn_decode.argtypes = [P, P, pc, P, P, pp, P, P, sz, P]
+    lib.paged_attn_decode_append.argtypes = [P, P, P, P, P, pc, P, P, pp, P, P, sz, P]
     lib.paged_attn_decode_noalloc.argtypes = [P, P, pc, P, P, pp, P, P]
     lib.paged_attn_decode_noalloc_capacity.argtypes = []
     lib.paged_attn_decode_noalloc_capacity.restype = sz
@@ -358,6 +360,42 @@ def paged_attn_decode(q: torch.Tensor, cache: PagedKVCache, block_table: torch.T
     _check(lib.paged_attn_decode(_ptr(q), _ptr(q_rope), ctypes.byref(d), _ptr(_i32(block_table)),
                                  _ptr(_i32(seq_lens)), ctypes.byref(p), _ptr(out), _ptr(workspace),
                                  ws_bytes, _stream(stream)))
+    return out
+
+
+def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: Optional[torch.Tensor],
+                             cache: PagedKVCache, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                             scale: float, window: int = 0, q_rope: Optional[torch.Tensor] = None,
+                             k_rope_new: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                             out_dtype: Optional[torch.dtype] = None, split_tokens: int = 0,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Write each sequence's newest K/V row (k_new, v_new [B, H_kv, D]; k_rope_new [B, 1, R]
+    for MLA) at position seq_lens[b] - 1, then decode as paged_attn_decode: one launch on
+    the bf16 stream-split path."""
+    B, H, D = q.shape
+    _check_attn_shapes(cache, q, q_rope, block_table, B, out)
+    _expect(seq_lens, (B,), "seq_lens")
+    _, _, hkv, hd = cache.k_cache.shape
+    _expect(k_new, (B, hkv, hd), "k_new")
+    _expect(v_new, (B, hkv, hd), "v_new")
+    if k_rope_new is not None:
+        _expect(k_rope_new, (B, hkv, cache.k_rope_cache.shape[3]), "k_rope_new")
+    _check_elems(cache, q, q_rope, k_new, v_new, k_rope_new)
+    if out is None:
+        out = torch.empty((B, H, D), dtype=out_dtype or q.dtype, device=q.device)
+    d = cache.desc()
+    p = _params(B, H, block_table, scale, window, _dtype_code(out), split_tokens)
+    if _check_indices:
+        from . import checks
+        _run_check(checks.check_append, block_table, seq_lens, d.block_size, d.num_blocks, int(window))
+    lib = load()
+    need = int(lib.paged_attn_decode_workspace(ctypes.byref(p), ctypes.byref(d)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.paged_attn_decode_append(_ptr(q), _ptr(q_rope), _ptr(k_new), _ptr(v_new), _ptr(k_rope_new),
+                                        ctypes.byref(d), _ptr(_i32(block_table)), _ptr(_i32(seq_lens)),
+                                        ctypes.byref(p), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

@@ -108,6 +108,18 @@ def check_decode(block_table, seq_lens, block_size: int, num_blocks: int, window
         _visible_blocks(bt[b], lo, int(L[b]), block_size, num_blocks, f"sequence {b}")
 
 
+def check_append(block_table, seq_lens, block_size: int, num_blocks: int, window: int = 0) -> None:
+    """paged_attn_decode_append: the decode's rules, and the newest slots (position
+    seq_lens[b] - 1 of every non-empty sequence) are distinct."""
+    check_decode(block_table, seq_lens, block_size, num_blocks, window)
+    bt = _host(block_table).astype(np.int64)
+    L = _host(seq_lens).astype(np.int64).ravel()
+    live = np.flatnonzero(L > 0)
+    p = L[live] - 1
+    slots = bt[live, p // block_size] * block_size + p % block_size
+    check_slots(slots, num_blocks * block_size)
+
+
 def check_prefill(block_table, cu_seqlens_q, seq_lens_kv, total_q: int, max_q_len: int, block_size: int,
                   num_blocks: int, window: int = 0) -> None:
     """paged_attn_prefill: cu_seqlens_q starts at 0, never decreases and ends at total_q;

@@ -216,12 +216,13 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
 
 // Prefill key split.  A prefill workgroup takes 128 query columns of one
 // (sequence, KV head) and walks every key they see; with few such workgroups
-// (multi-token decode: a handful of rows per sequence) the chip is not filled and
-// the longest sequence sets the time.  Then the keys are cut into partitions,
+// (short chunks: a handful of rows per sequence, more (row, head) columns per KV
+// head than the decode's stream split takes) the chip is not filled and the
+// longest sequence sets the time.  Then the keys are cut into partitions,
 // enough for about 16 workgroups per CU (ragged lengths leave many partitions
 // empty), of at least 2048 keys so that the fp32 partials stay a small fraction
 // of the K/V bytes (8, 32 and 64 per CU, and 1024- or 512-key partitions, measured
-// slower on the 70B multi-token decode).  The plan uses only what the
+// slower on the 70B multi-token decode when it ran here).  The plan uses only what the
 // workspace query also knows (rows per sequence from total_q, keys from the table
 // width), so both see the same partitions.
 struct PrefillPlan {
@@ -282,9 +283,15 @@ pkv_status static_scratch_ptr(void** out) {
   return PKV_OK;
 }
 
+// The newest K / V (/ rope) row of every sequence, for paged_attn_decode_append.
+struct AppendRows {
+  const void* k;
+  const void* v;
+  const void* k_rope;
+};
 pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache* cache, const int32_t* block_table,
                        const int32_t* seq_lens, const pkv_attn_params* params, void* out, void* workspace,
-                       size_t workspace_bytes, void* stream, bool static_scratch);
+                       size_t workspace_bytes, void* stream, bool static_scratch, const AppendRows* app = nullptr);
 
 pkv_status write_impl(const pkv::SlotSource& slots, int32_t num_tokens, const void* k, const void* v,
                       const void* k_rope, const pkv_paged_cache* cache, void* stream) {
@@ -448,6 +455,15 @@ pkv_status paged_attn_decode_noalloc(const void* q, const void* q_rope, const pk
   return decode_impl(q, q_rope, cache, block_table, seq_lens, params, out, nullptr, 0, stream, true);
 }
 
+pkv_status paged_attn_decode_append(const void* q, const void* q_rope, const void* k_new, const void* v_new,
+                                    const void* k_rope_new, const pkv_paged_cache* cache, const int32_t* block_table,
+                                    const int32_t* seq_lens, const pkv_attn_params* params, void* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  const AppendRows app{k_new, v_new, k_rope_new};
+  return decode_impl(q, q_rope, cache, block_table, seq_lens, params, out, workspace, workspace_bytes, stream, false,
+                     &app);
+}
+
 size_t paged_attn_decode_noalloc_capacity(void) { return kStaticScratchBytes; }
 
 }  // extern "C"
@@ -456,7 +472,7 @@ namespace {
 
 pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache* cache, const int32_t* block_table,
                        const int32_t* seq_lens, const pkv_attn_params* params, void* out, void* workspace,
-                       size_t workspace_bytes, void* stream, bool static_scratch) {
+                       size_t workspace_bytes, void* stream, bool static_scratch, const AppendRows* app) {
   pkv_status s = check_cache(cache);
   if (s) return s;
   s = check_params(params, cache);
@@ -485,6 +501,29 @@ pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache*
                 workspace ? workspace_bytes : (size_t)0);
   if (plan.ws_bytes > 0 && !aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  // Append: the bf16 stream split reads each sequence's newest row from the
+  // caller's rows and stores it at its slot inside the decode kernel; every other
+  // path writes the rows first (the writer of kv_cache_write_at, positions
+  // seq_lens[b] - 1) and then runs the decode unchanged.
+  const bool fused_append = app && plan.stream && cache->dtype == PKV_BF16;
+  if (app) {
+    const bool shared_kv = cache->v_cache == cache->k_cache;
+    if (!app->k || (!shared_kv && !app->v) || (shared_kv && app->v))
+      return fail(PKV_ERR_INVALID_ARG, "append: k_new is required, v_new exactly when v_cache is its own tensor");
+    if ((app->k_rope != nullptr) != is_mla(cache))
+      return fail(PKV_ERR_INVALID_ARG, "append: k_rope_new must be given exactly when the cache has a rope part");
+    if (!aligned16(app->k) || (app->v && !aligned16(app->v)) || (app->k_rope && !aligned16(app->k_rope)))
+      return fail(PKV_ERR_INVALID_ARG, "append: k_new / v_new / k_rope_new must be 16-byte aligned");
+    if (!fused_append) {
+      pkv::SlotSource src{};
+      src.block_table = block_table;
+      src.append_lens = seq_lens;
+      src.max_blocks_per_seq = params->max_blocks_per_seq;
+      src.block_size_log2 = log2i(cache->block_size);
+      s = write_impl(src, params->batch, app->k, app->v, app->k_rope, cache, stream);
+      if (s) return s;
+    }
+  }
   char* wsb = static_cast<char*>(workspace);
   float* ws_o = plan.ws_bytes > 0 ? reinterpret_cast<float*>(wsb + plan.ws_o_offset) : nullptr;
   float* ws_ml = plan.ws_bytes > 0 ? reinterpret_cast<float*>(wsb + plan.ws_ml_offset) : nullptr;
@@ -549,6 +588,10 @@ pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache*
   a.out_dtype = params->out_dtype;
   a.k_scale = static_cast<const float*>(cache->k_scale);
   a.v_scale = static_cast<const float*>(cache->v_scale);
+  if (fused_append) {
+    a.k_new = app->k;
+    a.v_new = app->v;
+  }
   if (plan.stream) {
     // bf16 with 128-wide heads: matrix-core decode over a stream split (any head
     // group: the group is a dense contraction and every K/V row is read once).

@@ -404,36 +404,66 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
           load_lds16(scale_src + ((((int64_t)phys * Hkv + g) << bs_log2) + (j & bs_mask)), sdst);
         }
       }
-    } else if constexpr (ONE_BLOCK) {  // one table entry, a wave-uniform base and 32-bit lane offsets
-      const int32_t phys = sload(bt + (t0 >> bs_log2));
-      const int64_t row0 = ((int64_t)phys << bs_log2) + (t0 & bs_mask);
-      const uint16_t* kb = kcache + row0 * row_elems + head_off;
-      const uint16_t* vb = vcache + row0 * row_elems + head_off;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t row = (uint32_t)min(max(4 * i + lg, lo_r), hi_r) * row_bytes;
-        load_lds16_s(kb, row + k_src[i & 3], kdst + 1024 * i);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t row = (uint32_t)min(max(4 * i + lg, lo_r), hi_r) * row_bytes;
-        load_lds16_s(vb, row + v_src[i & 1], vdst + 1024 * i);
-      }
     } else {
-      // 16-token blocks: the tile spans blocks blk and blk + 1 (the second only
-      // if it holds a visible key); both entries are scalar reads.
-      const int blk = t0 >> bs_log2;
-      const int32_t e0 = sload(bt + blk);
-      const int32_t e1 = ((blk + 1) << bs_log2) < c.L ? sload(bt + blk + 1) : e0;
+      // Append fused in: the sequence's newest key (row rn of this tile) comes
+      // from k_new / v_new rather than the cache, and this wave -- the only one
+      // that reads that row of KV head g -- stores it at its slot.  Nothing in
+      // this kernel reads the slot, so the store needs no ordering.
+      bool has_new = false;
+      int rn = 0;
+      if constexpr (!MT) {
+        rn = c.L - 1 - t0;
+        has_new = a.k_new != nullptr && rn >= 0 && rn < kKeyTile;
+      }
+      if (ONE_BLOCK && !has_new) {  // one table entry, a wave-uniform base and 32-bit lane offsets
+        const int32_t phys = sload(bt + (t0 >> bs_log2));
+        const int64_t row0 = ((int64_t)phys << bs_log2) + (t0 & bs_mask);
+        const uint16_t* kb = kcache + row0 * row_elems + head_off;
+        const uint16_t* vb = vcache + row0 * row_elems + head_off;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int j = t0 + min(max(4 * i + lg, lo_r), hi_r);
-        const int32_t phys = (j >> bs_log2) == blk ? e0 : e1;
-        const int64_t slot = ((int64_t)phys << bs_log2) + (j & bs_mask);
-        const unsigned char* kr = reinterpret_cast<const unsigned char*>(kcache + slot * row_elems + head_off);
-        const unsigned char* vr = reinterpret_cast<const unsigned char*>(vcache + slot * row_elems + head_off);
-        load_lds16(kr + k_src[i & 3], kdst + 1024 * i);
-        load_lds16(vr + v_src[i & 1], vdst + 1024 * i);
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t row = (uint32_t)min(max(4 * i + lg, lo_r), hi_r) * row_bytes;
+          load_lds16_s(kb, row + k_src[i & 3], kdst + 1024 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t row = (uint32_t)min(max(4 * i + lg, lo_r), hi_r) * row_bytes;
+          load_lds16_s(vb, row + v_src[i & 1], vdst + 1024 * i);
+        }
+      } else {
+        // Per-lane addresses: 16-token blocks (the tile spans blocks blk and
+        // blk + 1, the second only if it holds a visible key; both entries are
+        // scalar reads), or the tile holding the newest key.
+        const int blk = t0 >> bs_log2;
+        const int32_t e0 = sload(bt + blk);
+        const int32_t e1 = ((blk + 1) << bs_log2) < c.L ? sload(bt + blk + 1) : e0;
+        const int64_t new_off = ((int64_t)c.b * a.num_kv_heads + g) * kD * 2;  // bytes
+        const unsigned char* kn = has_new ? static_cast<const unsigned char*>(a.k_new) + new_off : nullptr;
+        const unsigned char* vn = has_new ? static_cast<const unsigned char*>(a.v_new) + new_off : nullptr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = min(max(4 * i + lg, lo_r), hi_r);
+          const int j = t0 + r;
+          const int32_t phys = (j >> bs_log2) == blk ? e0 : e1;
+          const int64_t slot = ((int64_t)phys << bs_log2) + (j & bs_mask);
+          const bool from_new = has_new && r == rn;
+          const unsigned char* kr =
+              from_new ? kn : reinterpret_cast<const unsigned char*>(kcache + slot * row_elems + head_off);
+          const unsigned char* vr =
+              from_new ? vn : reinterpret_cast<const unsigned char*>(vcache + slot * row_elems + head_off);
+          load_lds16(kr + k_src[i & 3], kdst + 1024 * i);
+          load_lds16(vr + v_src[i & 1], vdst + 1024 * i);
+        }
+        if (has_new && lane < 32) {
+          const int j = c.L - 1;
+          const int32_t phys = (j >> bs_log2) == blk ? e0 : e1;
+          const int64_t slot = ((int64_t)phys << bs_log2) + (j & bs_mask);
+          // The cache is the caller's writable memory; DecodeArgs carries it const
+          // because no other path of this kernel writes it.
+          uint16_t* dst = const_cast<uint16_t*>(lane < 16 ? kcache : vcache) + slot * row_elems + head_off;
+          const unsigned char* src = lane < 16 ? kn : vn;
+          st16(dst + 8 * l16, ld16(src + 16 * l16));
+        }
       }
     }
   };

@@ -29,6 +29,9 @@ struct SlotSource {
   const int32_t* block_table;
   const int32_t* batch_idx;
   const int32_t* pos;
+  // non-null: row t is the newest token of sequence t, at position append_lens[t] - 1
+  // (a length of 0 writes nothing); batch_idx and pos are then unused
+  const int32_t* append_lens;
   int32_t* slots_out;
   int32_t max_blocks_per_seq, block_size_log2;
 };
@@ -98,6 +101,12 @@ struct DecodeArgs {
   // null in decode.  total_q: all rows.
   const int32_t* cu_seqlens_q;
   int32_t total_q;
+  // Decode with the step's append fused in (bf16 stream split): each sequence's
+  // newest K and V rows [batch, num_kv_heads, 128].  The key at position
+  // seq_lens[b] - 1 is read from here instead of the cache, and the wave that
+  // reads it also stores it at its slot.  Null otherwise.
+  const void* k_new;
+  const void* v_new;
 };
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);

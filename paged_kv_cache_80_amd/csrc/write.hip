@@ -28,12 +28,14 @@ __global__ __launch_bounds__(256) void resolve_slots_kernel(const int32_t* __res
   slots[i] = (blk << bs_log2) + (p & ((1 << bs_log2) - 1));
 }
 
-// Slot of row t: given, or resolved from (batch_idx[t], pos[t]) as above.
+// Slot of row t: given, or resolved from (batch_idx[t], pos[t]) as above, or --
+// appending -- from (t, append_lens[t] - 1).
 __device__ __forceinline__ int32_t slot_of(const SlotSource& s, int64_t t) {
   if (s.slot_mapping) return s.slot_mapping[t];
-  const int32_t p = s.pos[t];
+  const int32_t p = s.append_lens ? s.append_lens[t] - 1 : s.pos[t];
   if (p < 0) return -1;
-  const int32_t blk = s.block_table[(int64_t)s.batch_idx[t] * s.max_blocks_per_seq + (p >> s.block_size_log2)];
+  const int64_t b = s.append_lens ? t : (int64_t)s.batch_idx[t];
+  const int32_t blk = s.block_table[b * s.max_blocks_per_seq + (p >> s.block_size_log2)];
   return (blk << s.block_size_log2) + (p & ((1 << s.block_size_log2) - 1));
 }
 

@@ -97,6 +97,22 @@ def test_decode_rope_both_or_neither(lib):
     assert "together" in lib.pkv_last_error().decode()
 
 
+def test_append_rejects_malformed_rows(lib):
+    """paged_attn_decode_append checks its new rows before anything is written or launched."""
+    c, p = _cache(), _params()
+
+    def call(k_new, v_new, k_rope_new=None, cache=c, q_rope=None):
+        return lib.paged_attn_decode_append(FAKE, q_rope, k_new, v_new, k_rope_new, ctypes.byref(cache), FAKE, FAKE,
+                                            ctypes.byref(p), FAKE, FAKE, 1 << 30, None)
+    assert call(None, FAKE) == 1 and "k_new" in lib.pkv_last_error().decode()
+    assert call(FAKE, None) == 1 and "v_new" in lib.pkv_last_error().decode()
+    assert call(FAKE + 8, FAKE) == 1 and "aligned" in lib.pkv_last_error().decode()
+    assert call(FAKE, FAKE, k_rope_new=FAKE) == 1 and "k_rope_new" in lib.pkv_last_error().decode()
+    mla = _cache(rope_dim=64, k_rope_cache=FAKE + 0x2000, v_cache=FAKE, num_kv_heads=1, head_dim=512)
+    assert call(FAKE, FAKE, FAKE, cache=mla, q_rope=FAKE) == 1  # v_new with a shared latent
+    assert "v_new" in lib.pkv_last_error().decode()
+
+
 def test_decode_workspace_too_small(lib):
     c, p = _cache(), _params(split_tokens=128)
     need = lib.paged_attn_decode_workspace(ctypes.byref(p), ctypes.byref(c))

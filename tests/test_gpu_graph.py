@@ -26,6 +26,8 @@ from gpu_util import DeviceCase  # noqa: E402
 CASES = {
     "bf16 GQA decode, window": lambda: workloads.decode_case(5, 8, 32, 8, 128, "bf16", block_size=32, max_blocks=40,
                                                              len_range=(1, 1200), window=500, null_block=True),
+    "append: bf16 GQA decode with its write fused in": lambda: workloads.decode_case(
+        12, 8, 32, 8, 128, "bf16", block_size=64, max_blocks=40, len_range=(1, 2500), null_block=True),
     "int8 MHA decode": lambda: workloads.decode_case(6, 4, 16, 16, 128, "bf16", block_size=64, max_blocks=20,
                                                      len_range=(1, 1200), int8=True),
     "fp32 decode (partition kernels)": lambda: workloads.decode_case(7, 3, 8, 2, 128, "f32", block_size=16,
@@ -64,6 +66,10 @@ def test_step_replays_in_a_graph(name):
     max_q = int(np.diff(case.cu_seqlens_q).max(initial=0)) if case.kind == "prefill" else 1
 
     def step():
+        if name.startswith("append"):  # write and decode in one kernel
+            pkv.paged_attn_decode_append(d.q, d.new_k, d.new_v, d.cache, d.block_table, d.seq_lens, case.scale,
+                                         case.window, out=out, workspace=ws)
+            return
         if name.startswith("bf16"):  # index resolution fused into the write
             pkv.kv_cache_write_at(d.block_table, d.new_batch_idx, d.new_pos, d.new_k, d.new_v, d.cache,
                                   k_rope=d.new_k_rope, slots_out=slots)

@@ -131,3 +131,14 @@ def test_write_at_checks():
         checks.check_write_at(np.array([[1, 1]], dtype=np.int32), 4, np.array([0, 0]), np.array([1, 5]), num_blocks=2)
     with pytest.raises(checks.IndexCheckError, match="block id"):
         checks.check_write_at(bt, 4, np.array([1]), np.array([4]), num_blocks=3)
+
+
+def test_append_checks():
+    """paged_attn_decode_append: the decode's rules, and no two sequences append at one slot."""
+    bt = np.array([[2, 0], [1, 3]], dtype=np.int32)
+    checks.check_append(bt, np.array([6, 3]), 4, num_blocks=4)
+    checks.check_append(bt, np.array([0, 3]), 4, num_blocks=4)  # an empty sequence appends nothing
+    with pytest.raises(checks.IndexCheckError, match="twice"):  # both newest keys in slot 1 * 4 + 1
+        checks.check_append(np.array([[1, 0], [1, 0]], dtype=np.int32), np.array([2, 2]), 4, num_blocks=4)
+    with pytest.raises(checks.IndexCheckError, match="table width"):
+        checks.check_append(bt, np.array([9, 1]), 4, num_blocks=4)
