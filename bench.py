@@ -520,7 +520,7 @@ def fused_append(case) -> bool:
             and case.D == 128 and case.G <= 16)
 
 
-def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass, graph=None):
+def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass, graph=None, warm_every_copy=False):
     """Time `steps` steps of one workload after `warmup` untimed ones, on cold-cache copies;
     returns the result fields of the JSON line.  A step is the append fused into the decode
     (one call) where the library fuses it, else the write (slots resolved in the writer)
@@ -580,6 +580,8 @@ def measure(args, case, torch, pkv, steps, warmup, cpu_seconds, warm_pass, graph
         if e1 is not None:
             e1.record()
 
+    if warm_every_copy:  # short runs: every cache copy is touched once before the timed steps
+        warmup = max(warmup, len(caches))
     ms_step, ms_attn, med_attn = _timed(torch, step, steps, warmup)
     warm = _timed(torch, lambda i, e0=None, e1=None: step(0, e0, e1), steps, warmup) if warm_pass else None
     graph_ms = graph_step_ms(torch, step, steps) if (warm_pass if graph is None else graph) else None
@@ -766,7 +768,8 @@ def main():
             c = workloads.WORKLOADS[other](args.seed)
             c.seed_label = args.seed
             r = measure(args, c, torch, pkv, args.map_steps, 3,
-                        0.0 if args.no_cpu_baseline else args.map_cpu_seconds, False, graph=True)
+                        0.0 if args.no_cpu_baseline else args.map_cpu_seconds, False, graph=True,
+                        warm_every_copy=True)
             del c
             torch.cuda.empty_cache()
             wl[other] = map_entry(r, ceiling)
