@@ -43,6 +43,7 @@ constexpr int kKeyTile = 64;                     // keys per LDS tile
 constexpr int kMaxTableLds = kPrefillMaxTableBlocks;  // block-table entries staged in LDS
 static_assert(kCols == kPrefillColumns && kKeyTile == kPrefillKeyTile, "host sizing");
 constexpr float kRescaleLog2 = 8.f;              // lazy-rescale threshold (log2 units)
+constexpr float kRaiseSum = 256.f;               // 2^kRescaleLog2: a lane sum at most this has no p above it
 
 template <int D>
 struct Tile {
@@ -288,35 +289,50 @@ __global__ __launch_bounds__(kWaves * kWave, 2) void prefill_mfma_kernel(Prefill
           }
         }
       }
-      // A running chain of pairs, so that each step is one v_max3_f32.
-      float mt = s[ct][0][0];
+      // Probabilities against the current reference, and this lane's sum of them.
+      // No lane's sum above 2^8 means no probability above 2^8, i.e. no logit past
+      // the reference by more than the rescale threshold: the raise test needs the
+      // column maximum (a max chain and a cross-row exchange) only when some lane's
+      // sum says it might -- the first visible tile, a new peak -- and then the
+      // probabilities are taken again against the raised reference.  The decision
+      // is the one the maximum alone would take.
+      auto probs = [&](float mb, float& ls) {
+        ls = 0.f;
 #pragma unroll
-      for (int e = 1; e + 1 < 4 * NU; e += 2)
-        mt = fmaxf(fmaxf(mt, s[ct][e / 4][e % 4]), s[ct][(e + 1) / 4][(e + 1) % 4]);
-      mt = fmaxf(mt, s[ct][NU - 1][3]);
-      const float mts = row4_max(mt) * c2;
-      const bool raise = mts > mref[ct] + kRescaleLog2;
-      if (__any(raise)) {
-        const float alpha = raise ? exp2_fast(mref[ct] - mts) : 1.f;  // mref = -inf gives 0
-        if (raise) mref[ct] = mts;
-        l[ct] *= alpha;
+        for (int kk = 0; kk < kKeyTile / 32; ++kk) {
+          float p8[8];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float p = exp2_fast(fmaf(s[ct][2 * kk + h][r], c2, -mb));
+              p8[4 * h + r] = p;
+              ls += p;
+            }
+          pack_p_split(p8, phi[ct][kk], plo[ct][kk]);
+        }
+      };
+      float ls;
+      probs(mref[ct] == kNegInf ? 0.f : mref[ct], ls);
+      if (__any(mref[ct] == kNegInf || !(ls <= kRaiseSum))) {  // !(<=): a NaN or inf sum too
+        // A running chain of pairs, so that each step is one v_max3_f32.
+        float mt = s[ct][0][0];
+#pragma unroll
+        for (int e = 1; e + 1 < 4 * NU; e += 2)
+          mt = fmaxf(fmaxf(mt, s[ct][e / 4][e % 4]), s[ct][(e + 1) / 4][(e + 1) % 4]);
+        mt = fmaxf(mt, s[ct][NU - 1][3]);
+        const float mts = row4_max(mt) * c2;
+        const bool raise = mts > mref[ct] + kRescaleLog2;
+        if (__any(raise)) {
+          const float alpha = raise ? exp2_fast(mref[ct] - mts) : 1.f;  // mref = -inf gives 0
+          if (raise) mref[ct] = mts;
+          l[ct] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+        }
+        probs(mref[ct] == kNegInf ? 0.f : mref[ct], ls);  // no visible key yet: every p is 0
       }
-      const float mb = mref[ct] == kNegInf ? 0.f : mref[ct];  // no visible key yet: every p is 0
-#pragma unroll
-      for (int kk = 0; kk < kKeyTile / 32; ++kk) {
-        float p8[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = exp2_fast(fmaf(s[ct][2 * kk + h][r], c2, -mb));
-            p8[4 * h + r] = p;
-            l[ct] += p;
-          }
-        pack_p_split(p8, phi[ct][kk], plo[ct][kk]);
-      }
+      l[ct] += ls;
     }
     __builtin_amdgcn_sched_barrier(0);
 
