@@ -72,6 +72,7 @@ constexpr int kRowBytes = kD * 2;                 // 256: one head row of K or V
 constexpr int kWaves = 4;                         // independent waves per workgroup (bf16)
 constexpr int kWavesI8 = 8;                       // int8: half-size slots leave LDS for twice the waves
 constexpr float kRescaleLog2 = 8.f;
+constexpr float kRaiseSum = 256.f;  // 2^kRescaleLog2: a lane sum at most this has no p above it
 
 // Tile geometry per cache type: bytes of one head row, of one tensor of a tile,
 // of a whole LDS slot (K, V and, for int8, the tile's 32 + 32 scales), and the
@@ -577,30 +578,40 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
         }
       }
     }
-    float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mt = row4_max(mt);
-    const float mts = mt * c2;
-    const bool raise = mts > mref[0] + kRescaleLog2;
-    if (__any(raise)) {
-      const float alpha = raise ? exp2_fast(mref[0] - mts) : 1.f;
-      if (raise) mref[0] = mts;
-      l[0] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[0][dt] *= alpha;
-    }
-    const float mb = mref[0] == kNegInf ? 0.f : mref[0];
+    // Probabilities against the current reference first; the column maximum is
+    // formed only when some lane's sum of them says it may be needed (see compute).
     float pv[8];
+    float ls;
+    auto probs = [&](float mb) {
+      ls = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float* vs = reinterpret_cast<const float*>(&vsc[u]);
+      for (int u = 0; u < 2; ++u) {
+        const float* vs = reinterpret_cast<const float*>(&vsc[u]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = exp2_fast(fmaf(s[u][e], c2, -mb));
-        l[0] += p;
-        pv[4 * u + e] = p * vs[e];
+        for (int e = 0; e < 4; ++e) {
+          const float p = exp2_fast(fmaf(s[u][e], c2, -mb));
+          ls += p;
+          pv[4 * u + e] = p * vs[e];
+        }
       }
+    };
+    probs(mref[0] == kNegInf ? 0.f : mref[0]);
+    if (__any(mref[0] == kNegInf || !(ls <= kRaiseSum))) {
+      float mt = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      mt = row4_max(mt);
+      const float mts = mt * c2;
+      const bool raise = mts > mref[0] + kRescaleLog2;
+      if (__any(raise)) {
+        const float alpha = raise ? exp2_fast(mref[0] - mts) : 1.f;
+        if (raise) mref[0] = mts;
+        l[0] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[0][dt] *= alpha;
+      }
+      probs(mref[0] == kNegInf ? 0.f : mref[0]);
     }
+    l[0] += ls;
     uint4 phi, plo;
     pack_p_split(pv, phi, plo);
 #pragma unroll
@@ -657,28 +668,42 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
     uint4 phi[CT], plo[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      float mt = fmaxf(fmaxf(fmaxf(s[ct][0][0], s[ct][0][1]), fmaxf(s[ct][0][2], s[ct][0][3])),
-                       fmaxf(fmaxf(s[ct][1][0], s[ct][1][1]), fmaxf(s[ct][1][2], s[ct][1][3])));
-      mt = row4_max(mt);
-      const float mts = mt * c2;
-      const bool raise = mts > mref[ct] + kRescaleLog2;
-      if (__any(raise)) {
-        const float alpha = raise ? exp2_fast(mref[ct] - mts) : 1.f;  // mref = -inf gives 0
-        if (raise) mref[ct] = mts;
-        l[ct] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
-      }
-      const float mb = mref[ct] == kNegInf ? 0.f : mref[ct];  // no finite logit yet: every p is 0
+      // Probabilities against the current reference and this lane's sum of them.
+      // No lane's sum above 2^8 means no probability above 2^8 (no logit past the
+      // reference by more than the rescale threshold), so the column maximum --
+      // a max chain and the cross-row exchange -- is formed only when some sum
+      // says it may be needed (the first visible tile, a new peak); the
+      // probabilities are then taken again against the raised reference.
       float p8[8];
+      float ls;
+      auto probs = [&](float mb) {
+        ls = 0.f;
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = exp2_fast(fmaf(s[ct][u][e], c2, -mb));
-          p8[4 * u + e] = p;
-          l[ct] += p;
+          for (int e = 0; e < 4; ++e) {
+            const float p = exp2_fast(fmaf(s[ct][u][e], c2, -mb));
+            p8[4 * u + e] = p;
+            ls += p;
+          }
+      };
+      probs(mref[ct] == kNegInf ? 0.f : mref[ct]);
+      if (__any(mref[ct] == kNegInf || !(ls <= kRaiseSum))) {  // !(<=): a NaN or inf sum too
+        float mt = fmaxf(fmaxf(fmaxf(s[ct][0][0], s[ct][0][1]), fmaxf(s[ct][0][2], s[ct][0][3])),
+                         fmaxf(fmaxf(s[ct][1][0], s[ct][1][1]), fmaxf(s[ct][1][2], s[ct][1][3])));
+        mt = row4_max(mt);
+        const float mts = mt * c2;
+        const bool raise = mts > mref[ct] + kRescaleLog2;
+        if (__any(raise)) {
+          const float alpha = raise ? exp2_fast(mref[ct] - mts) : 1.f;  // mref = -inf gives 0
+          if (raise) mref[ct] = mts;
+          l[ct] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
         }
+        probs(mref[ct] == kNegInf ? 0.f : mref[ct]);  // no finite logit yet: every p is 0
+      }
+      l[ct] += ls;
       pack_p_split(p8, phi[ct], plo[ct]);
     }
 #pragma unroll

@@ -41,6 +41,7 @@ constexpr int kPvAhead = 2;
 // the stale reference, which is exact (o and l share it) and skips the O
 // rescale on almost every tile.
 constexpr float kRescaleLog2 = 8.f;
+constexpr float kRaiseSum = 256.f;  // 2^kRescaleLog2: a lane sum at most this has no p above it
 
 __device__ __forceinline__ int rope_swz(int r) { return r & 7; }
 
@@ -246,31 +247,41 @@ __global__ __launch_bounds__(NW * kWave, 8 / NW) void mla_decode_kernel(MlaArgs 
           s[u][r] = (j >= tok_begin && j < tok_end) ? s[u][r] : kNegInf;
         }
     }
-    float mt = kNegInf;
-#pragma unroll
-    for (int u = 0; u < kKeyTile / 16; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[u][r]);
-    const float mts = row4_max(mt) * c2;
-    const bool raise = mts > mref + kRescaleLog2;
-    if (__any(raise)) {
-      const float alpha = raise ? exp2_fast(mref - mts) : 1.f;  // mref = -inf gives 0
-      if (raise) mref = mts;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-    const float mb = mref == kNegInf ? 0.f : mref;  // no finite score yet: every p is 0
+    // Probabilities against the current reference and this lane's sum of them; the
+    // column maximum (to raise the reference) is formed only when some lane's sum
+    // exceeds 2^8 -- which any probability above 2^8 implies -- and the
+    // probabilities are then taken again.
     float p8[8];
-    float ls = 0.f;
+    float ls;
+    auto probs = [&](float mb) {
+      ls = 0.f;
 #pragma unroll
-    for (int u = 0; u < kKeyTile / 16; ++u)
+      for (int u = 0; u < kKeyTile / 16; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2_fast(fmaf(s[u][r], c2, -mb));
-        p8[4 * u + r] = p;
-        ls += p;
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2_fast(fmaf(s[u][r], c2, -mb));
+          p8[4 * u + r] = p;
+          ls += p;
+        }
+    };
+    probs(mref == kNegInf ? 0.f : mref);
+    if (__any(mref == kNegInf || !(ls <= kRaiseSum))) {  // !(<=): a NaN or inf sum too
+      float mt = kNegInf;
+#pragma unroll
+      for (int u = 0; u < kKeyTile / 16; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[u][r]);
+      const float mts = row4_max(mt) * c2;
+      const bool raise = mts > mref + kRescaleLog2;
+      if (__any(raise)) {
+        const float alpha = raise ? exp2_fast(mref - mts) : 1.f;  // mref = -inf gives 0
+        if (raise) mref = mts;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
       }
+      probs(mref == kNegInf ? 0.f : mref);  // no finite score yet: every p is 0
+    }
     l += ls;
     uint4 phi, plo;
     pack_p_split(p8, phi, plo);
