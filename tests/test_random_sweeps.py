@@ -4,7 +4,8 @@ CPU: the oracle against the numpy brute force on 150 tiny decode and 100 tiny pr
 draws -- block sizes 4 / 16 / 128, MHA, GQA, MQA and MLA, windows including 1 and
 windows that cover every key, empty sequences, random pools and tables.
 GPU: 96 small calls of every kernel family through the C ABI against the oracle at the
-bars of the parity tests, stopping at the first mismatch with the case named."""
+bars of the parity tests (decode draws also as one paged_attn_decode_append call, bit for
+bit the write then the decode), stopping at the first mismatch with the case named."""
 import numpy as np
 import pytest
 
@@ -48,6 +49,7 @@ def test_kernels_match_oracle_on_random_calls(orc):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+    import paged_kv_cache_80_amd as pkv
     from gpu_util import DeviceCase, assert_rows_close
     for i in range(96):
         name, c, split = sweep_cases.gpu_case(i)
@@ -59,6 +61,13 @@ def test_kernels_match_oracle_on_random_calls(orc):
             out, _ = DeviceCase(c).run(out_dtype=torch.float32)
         try:
             assert_rows_close(out, ref, 1e-5 if c.dtype == "f32" else 1e-4)
+            if c.kind == "decode":  # the step as one call: bit for bit the write, then the decode
+                d = DeviceCase(c)
+                app = pkv.paged_attn_decode_append(d.q, d.new_k, d.new_v, d.cache, d.block_table, d.seq_lens,
+                                                   c.scale, c.window, q_rope=d.q_rope, k_rope_new=d.new_k_rope,
+                                                   out_dtype=torch.float32, split_tokens=split)
+                torch.cuda.synchronize()
+                assert torch.equal(app, out), "paged_attn_decode_append differs from write + decode"
             if c.dtype == "bf16":
                 out, _ = DeviceCase(c).run(split_tokens=split) if c.kind == "decode" else DeviceCase(c).run()
                 assert_rows_close(out, ref, 2e-3)
