@@ -129,6 +129,7 @@ struct DecodePlan {
   int32_t split_tiles;     // stream split: tiles per wave target (0 = all waves)
   int32_t bpp;             // partition split
   int32_t max_np;
+  int32_t valu_waves;      // vector-ALU decode: 4 per partition, 16 per whole sequence
   size_t ws_bytes;
   size_t ws_o_offset;
   size_t ws_ml_offset;
@@ -204,6 +205,16 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
   while ((span + bpp - 1) / bpp > 65535 && bpp < kMaxBpp) bpp = std::min(2 * bpp, kMaxBpp);
   plan.bpp = bpp;
   plan.max_np = (span + bpp - 1) / bpp;
+  plan.valu_waves = 4;
+  // A sequence cut into at most 4 partitions is walked by one 16-wave workgroup
+  // instead: the same keys per wave and iteration, merged in LDS rather than by
+  // a second kernel over partials (unless the caller asked for partitions).
+  if (!is_mla(c) && p->split_tokens == 0 && plan.max_np > 1 && plan.max_np <= 4 && span <= kMaxBpp &&
+      pkv::decode_valu_wide_supported(c->dtype, c->head_dim, p->num_q_heads / c->num_kv_heads)) {
+    plan.bpp = span;
+    plan.max_np = 1;
+    plan.valu_waves = 16;
+  }
   if (plan.max_np > 1) {
     const size_t rows = (size_t)p->batch * p->num_q_heads * plan.max_np;
     const size_t o_bytes = (rows * c->head_dim * sizeof(float) + 255) & ~size_t(255);
@@ -588,6 +599,7 @@ pkv_status decode_impl(const void* q, const void* q_rope, const pkv_paged_cache*
   a.out_dtype = params->out_dtype;
   a.k_scale = static_cast<const float*>(cache->k_scale);
   a.v_scale = static_cast<const float*>(cache->v_scale);
+  a.valu_waves = plan.valu_waves;
   if (fused_append) {
     a.k_new = app->k;
     a.v_new = app->v;

@@ -29,6 +29,14 @@ namespace pkv {
 namespace {
 
 constexpr int kWaves = 4;
+// A whole sequence per workgroup: 16 waves stream 4x the keys of a 4-wave
+// partition per iteration and merge in LDS, so a call that would cut each
+// sequence into at most 4 partitions runs as one kernel, with no partials and
+// no combine.  Only where the per-wave state fits, unspilled, the 128 registers
+// a lane has at 16 waves per CU: fp32 rows of up to 256 elements over the head
+// group (4 elements a lane chunk), bf16 (8 a chunk) with one head per KV head.
+constexpr int kWideWaves = 16;
+constexpr bool wide_fits(int elem_bytes, int D, int GT) { return elem_bytes == 4 ? GT * D <= 256 : GT == 1; }
 constexpr int kMaxBpp = 1024;  // table blocks per partition held in LDS
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -108,18 +116,18 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x, int32_t
     static_cast<float*>(out)[i] = x;
 }
 
-template <typename T, int D, int GT, int U>
-__global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs a) {
+template <typename T, int D, int GT, int U, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeArgs a) {
   constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane chunk
   constexpr int LPR = D / EPL;              // lanes per row
   constexpr int RPW = kWave / LPR;          // rows per wave load
-  constexpr int CH = kWaves * RPW * U;      // tokens per iteration
+  constexpr int CH = NW * RPW * U;          // tokens per iteration
   static_assert(LPR >= 1 && LPR <= kWave && (kWave % LPR) == 0, "row must fit a wave");
 
   __shared__ int32_t s_blk[kMaxBpp];
-  __shared__ float s_m[kWaves][GT];
-  __shared__ float s_l[kWaves][GT];
-  __shared__ float s_acc[kWaves][GT][D];
+  __shared__ float s_m[NW][GT];
+  __shared__ float s_l[NW][GT];
+  __shared__ float s_acc[NW][GT][D];
 
   // The grid is (KV head, sequence) x partition with the KV head fastest.
   // Workgroups are dealt to the 8 XCDs round-robin in launch order, so KV head
@@ -258,10 +266,10 @@ __global__ __launch_bounds__(kWaves * kWave) void decode_valu_kernel(DecodeArgs 
     const int d = i - h * D;
     float M = s_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
     float Ls = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = rescale(s_m[w][h], M);
       Ls += s_l[w][h] * f;
       O += s_acc[w][h][d] * f;
@@ -319,7 +327,14 @@ template <typename T, int D, int GT>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   constexpr int U = GT <= 2 ? 8 : 4;
   const dim3 grid(a.num_kv_heads * a.batch, a.max_np);
-  decode_valu_kernel<T, D, GT, U><<<grid, kWaves * kWave, 0, stream>>>(a);
+  if (a.valu_waves == kWideWaves) {
+    if constexpr (wide_fits((int)sizeof(T), D, GT)) {
+      decode_valu_kernel<T, D, GT, U, kWideWaves><<<grid, kWideWaves * kWave, 0, stream>>>(a);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
+  decode_valu_kernel<T, D, GT, U, kWaves><<<grid, kWaves * kWave, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -352,9 +367,15 @@ bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group) {
   return gt <= 16 && gt * head_dim <= 2048;
 }
 
+bool decode_valu_wide_supported(int32_t dtype, int32_t head_dim, int32_t group) {
+  return decode_valu_supported(dtype, head_dim, group) &&
+         wide_fits(dtype == PKV_F32 ? 4 : 2, head_dim, group_template(group));
+}
+
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
   const int gt = group_template(a.num_q_heads / a.num_kv_heads);
   if (a.blocks_per_part > kMaxBpp) return hipErrorInvalidValue;
+  if (a.valu_waves != kWaves && !(a.valu_waves == kWideWaves && a.max_np == 1)) return hipErrorInvalidValue;
   if (a.dtype == PKV_BF16) {
     switch (a.head_dim) {
       case 64: return launch_d<uint16_t, 64>(a, gt, stream);

@@ -18,10 +18,11 @@
 // start-up cost; waves are dealt to the 8 XCDs round robin, so every XCD streams
 // the same share; and the H_kv waves of a group read the same slot rows (one
 // row holds every head of a token) at about the same time, which keeps DRAM
-// pages open.  A run crosses sequence ends: the wave then stores the partial
-// (m, l, O) of the piece of sequence b it holds as piece (x + b) H_kv + g (a
-// group boundary and a sequence boundary never produce the same x + b), and
-// stream_combine merges the pieces of each output row.  Both kernels need the
+// pages open.  A run crosses sequence ends.  A sequence that the group holds
+// whole is normalised and stored by its waves; otherwise the wave stores the
+// partial (m, l, O) of the piece of sequence b it holds as piece (x + b)
+// H_kv + g (a group boundary and a sequence boundary never produce the same
+// x + b), and stream_combine merges the pieces of each output row.  Both kernels need the
 // per-sequence column prefix of seq_lens: each decode workgroup scans it into
 // LDS at start (workgroup 0 also stores it for the combine), or, for batches
 // of 2048 sequences and more, a small scan kernel writes it first.
@@ -510,13 +511,35 @@ __global__ __launch_bounds__((I8 ? kWavesI8 : kWaves) * kWave, 1) void decode_st
       l[ct] = 0.f;
     }
   };
-  // Store the partial of the piece of sequence c.b held, as piece (grp + b) H_kv + g
-  // (kStreamCols columns of a piece in multi-token decode, G in decode).
+  // The piece of sequence c.b that this wave holds is complete.  A sequence
+  // this group holds whole (its first and last columns in this run) is
+  // normalised and stored here, and the combine skips its rows; a piece of a
+  // split one is stored as piece (grp + b) H_kv + g (kStreamCols columns of a
+  // piece in multi-token decode, G in decode).
   auto flush = [&](const Cursor& c) {
+    const int64_t p0 = prefix_at(c.b);
+    const bool whole = group_of_column(p0, C, NG) == group_of_column(p0 + c.n - 1, C, NG);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const float lsum = row4_sum(l[ct]);
       if (!cvalid[ct]) continue;
+      if (whole) {
+        int64_t orow;
+        if constexpr (MT) {
+          const int col = 16 * ct + l16;
+          const int i = col / G;
+          orow = (int64_t)(c.q0 + i) * H + (int64_t)g * G + (col - i * G);
+        } else {
+          orow = (int64_t)c.q0 * H + (int64_t)g * G + l16;
+        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const float v[4] = {o[ct][dt][0] * inv, o[ct][dt][1] * inv, o[ct][dt][2] * inv, o[ct][dt][3] * inv};
+          store4(a.out, orow * kD + 16 * dt + 4 * lg, v, a.out_dtype);
+        }
+        continue;
+      }
       const int64_t prow = MT ? ((grp + c.b) * Hkv + g) * kStreamCols + 16 * ct + l16 : ((grp + c.b) * Hkv + g) * G + l16;
       float* wo = a.ws_o + prow * kD;
 #pragma unroll
@@ -800,6 +823,7 @@ __global__ __launch_bounds__(kWaves * kWave) void stream_combine_kernel(DecodeAr
     const int64_t C = prefix[a.batch];
     const int64_t NG = stream_groups(C, a.resident_waves, Hkv, a.split_tiles);
     const int64_t xA = group_of_column(p0, C, NG), xB = group_of_column(p0 + n - 1, C, NG);
+    if (xA == xB) return;  // one group held the sequence whole and stored its rows
     // Groups in [xA, xB] with an empty run (fewer columns than groups) store
     // nothing; every other one holds a piece of sequence b.
     auto piece_row = [&](int64_t x) { return ((x + b) * Hkv + g) * cols + c; };

@@ -107,9 +107,14 @@ struct DecodeArgs {
   // reads it also stores it at its slot.  Null otherwise.
   const void* k_new;
   const void* v_new;
+  // Vector-ALU decode only: waves per workgroup, 4 (a workgroup per partition of
+  // blocks_per_part blocks) or 16 (a workgroup per whole sequence, max_np == 1).
+  int32_t valu_waves;
 };
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 bool decode_valu_supported(int32_t dtype, int32_t head_dim, int32_t group);
+// Whether the 16-wave whole-sequence variant serves this shape.
+bool decode_valu_wide_supported(int32_t dtype, int32_t head_dim, int32_t group);
 // The same decode on the matrix cores with a stream split (decode_mfma.hip):
 // bf16 or int8 caches, head_dim 128, head groups up to 16.  Launches the tile scan, the decode
 // and the piece combine.

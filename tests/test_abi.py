@@ -136,20 +136,31 @@ def test_workspace_size_formula(lib):
 def test_small_vector_alu_decodes_take_short_partitions(lib):
     """The partition length of the vector-ALU decode when the caller gives none: 512 keys,
     shorter (down to 128) while B * H_kv workgroups per partition would leave CUs idle
-    (256 CUs assumed without a GPU).  The tiny fp32 decode (2 sequences x 4 KV heads, 4
-    blocks of 128) takes four 128-key partitions; 64 pairs take 128-key partitions as well
-    (64 x 4 workgroups); 512 pairs keep whole 512-key sequences (no workspace)."""
-    c = _cache(dtype=pkv.PKV_F32, num_kv_heads=4)
+    (256 CUs assumed without a GPU).  A sequence that this would cut into at most 4
+    partitions is walked by one 16-wave workgroup instead, with no partials (no
+    workspace): the tiny fp32 decode (2 sequences x 4 KV heads, 4 blocks of 128 -> four
+    128-key partitions) and 64 pairs of 512 keys; 8 blocks of 128 at 2 x 4 pairs make
+    eight 128-key partitions, which stay partitions; 512 pairs keep whole 512-key
+    sequences.  A caller's split_tokens always gives partitions."""
+    def ws(batch, heads, blocks=4, split=0, kv=4, dtype=pkv.PKV_F32, head_dim=128):
+        c = _cache(dtype=dtype, num_kv_heads=kv, head_dim=head_dim)
+        p = _params(batch=batch, num_q_heads=heads, max_blocks_per_seq=blocks, split_tokens=split)
+        return lib.paged_attn_decode_workspace(ctypes.byref(p), ctypes.byref(c))
 
-    def ws(batch, heads):
-        return lib.paged_attn_decode_workspace(ctypes.byref(_params(batch=batch, num_q_heads=heads)),
-                                               ctypes.byref(c))
+    def parts(rows, np_, d=128):
+        rows *= np_
+        return (rows * d * 4 + 255) // 256 * 256 + rows * 8
 
-    rows = 2 * 4 * 4
-    assert ws(2, 4) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
-    rows = 16 * 4 * 4
-    assert ws(16, 4) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
+    assert ws(2, 4) == 0
+    assert ws(16, 4) == 0
     assert ws(128, 4) == 0
+    assert ws(2, 4, blocks=8) == parts(2 * 4, 8)
+    assert ws(2, 4, split=128) == parts(2 * 4, 4)
+    # the 16-wave variant holds fp32 head groups up to 256 elements, bf16 single heads
+    assert ws(2, 8, kv=2, head_dim=64) == 0                        # fp32, G = 4, d = 64
+    assert ws(2, 8, kv=2, head_dim=128) == parts(2 * 8, 4)         # fp32, G = 4, d = 128
+    assert ws(2, 2, kv=2, dtype=pkv.PKV_BF16, head_dim=256) == 0   # bf16, G = 1
+    assert ws(2, 4, kv=2, dtype=pkv.PKV_BF16, head_dim=256) == parts(2 * 4, 4, 256)
 
 
 def test_stream_workspace_layout(lib):

@@ -178,6 +178,77 @@ def test_decode_matches_oracle(orc, shape, split):
     assert_rows_close(out, ref, F32_TOL if dt == "f32" else BF16_TOL)
 
 
+# The vector-ALU decode's whole-sequence variant: one 16-wave workgroup per (sequence, KV
+# head), its waves merged in LDS, taken when the planner would cut each sequence into at
+# most 4 partitions (small batches; fp32 head groups of up to 256 elements, bf16 single
+# heads).  The zero workspace the call asks for shows that variant ran.
+WIDE_MATRIX = [
+    # B, H, Hkv, D, dtype, bs, max_blocks, seq_lens or len_range, window
+    (3, 12, 3, 64, "f32", 32, 16, [0, 1, 512], 0),                  # G = 4, an empty sequence
+    (2, 6, 2, 64, "f32", 32, 16, (1, 512), 0),                      # G = 3, padded to 4
+    (8, 8, 4, 128, "f32", 16, 32, [1, 15, 16, 17, 255, 256, 257, 512], 0),  # G = 2, block edges
+    (5, 8, 4, 128, "f32", 64, 8, (1, 512), 100),                    # window over null-padded tables
+    (2, 4, 4, 256, "f32", 128, 4, (1, 512), 0),                     # d = 256
+    (4, 4, 4, 256, "bf16", 64, 8, (1, 512), 0),                     # bf16, d = 256
+    (6, 2, 2, 64, "bf16", 16, 32, (1, 512), 300),                   # bf16, d = 64, window
+    (16, 4, 4, 128, "f32", 128, 4, [512] * 16, 1),                  # window of one key
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_MATRIX)
+def test_whole_sequence_workgroups_match_oracle(orc, shape):
+    import paged_kv_cache_80_amd as pkv
+    B, H, Hkv, D, dt, bs, mb, lens, w = shape
+    kw = {"seq_lens": np.array(lens, dtype=np.int32)} if isinstance(lens, list) else {"len_range": lens}
+    case = workloads.decode_case(B * 37 + D, B, H, Hkv, D, dt, block_size=bs, max_blocks=mb, window=w,
+                                 null_block=True, **kw)
+    d = DeviceCase(case)
+    assert pkv.paged_attn_decode_workspace(d.cache, B, H, mb, case.scale, w) == 0
+    ref, _, _ = oracle_run(orc, case)
+    out, _ = d.run()
+    assert_rows_close(out, ref, F32_TOL if dt == "f32" else BF16_TOL)
+    out32 = d.attend(out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_rows_close(out32, ref, ACC_TOL)
+
+
+def test_split_sequences_merge_identically_call_after_call(orc):
+    """On the stream split, a sequence whose tiles span several wave groups leaves one
+    partial per group, which the combine merges; a sequence one group holds whole is
+    normalised and stored by the decode kernel, and the combine skips its rows.  Twenty
+    calls alternating two shapes with many split sequences (ragged lengths over 16-token
+    blocks; a window, empty sequences and 64-token blocks) share one workspace that starts
+    as random bytes, so every call meets partials that another call left: each shape's
+    outputs are bit-identical call after call, and the first matches the oracle."""
+    import paged_kv_cache_80_amd as pkv
+    a = workloads.decode_case(77, 16, 32, 8, 128, "bf16", block_size=16, max_blocks=200,
+                              len_range=(1, 3200), null_block=True)
+    lens_b = np.random.default_rng(78).integers(1, 2501, size=40).astype(np.int32)
+    lens_b[[0, 17, 39]] = 0
+    b = workloads.decode_case(78, 40, 16, 4, 128, "bf16", block_size=64, max_blocks=40,
+                              seq_lens=lens_b, window=700, null_block=True)
+    da, db = DeviceCase(a), DeviceCase(b)
+    for d in (da, db):  # the step's newest rows, which the oracle's decode sees
+        d.write(d.resolve())
+    need = max(pkv.paged_attn_decode_workspace(da.cache, a.B, a.H, 200, a.scale),
+               pkv.paged_attn_decode_workspace(db.cache, b.B, b.H, 40, b.scale, b.window))
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    outs = {0: [], 1: []}
+    for i in range(20):
+        k = i % 2
+        case, d = (a, da) if k == 0 else (b, db)
+        outs[k].append(pkv.paged_attn_decode(d.q, d.cache, d.block_table, d.seq_lens, case.scale, case.window,
+                                             out_dtype=torch.float32, workspace=ws))
+    torch.cuda.synchronize()
+    for k in (0, 1):
+        for j, o in enumerate(outs[k][1:], 1):
+            assert torch.equal(o, outs[k][0]), f"shape {k}: call {j} differs from the first"
+    ref_a, _, _ = oracle_run(orc, a)
+    ref_b, _, _ = oracle_run(orc, b)
+    assert_rows_close(outs[0][0], ref_a, ACC_TOL)
+    assert_rows_close(outs[1][0], ref_b, ACC_TOL)
+
+
 @pytest.mark.parametrize("split_blocks", [1, 2, 7, 0])
 def test_split_count_invariance(orc, split_blocks):
     """Splitting the keys over 1..N workgroups and merging (m, l, o) is exact algebra; every
