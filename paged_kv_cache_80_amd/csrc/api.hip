@@ -190,9 +190,9 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
     } else {
       // At most 512 keys a partition (2048 with 1024 or more (sequence, KV head)
       // pairs), fewer -- down to 128 -- while that would leave CUs without a
-      // workgroup: a tiny decode (2 sequences x 4 heads of up to 512 keys) is
-      // otherwise 8 workgroups each walking a whole sequence, and takes 11.3 us
-      // against 7.9 us as 32 partitions plus the combine.
+      // workgroup (a tiny decode, 2 sequences x 4 heads of up to 512 keys, took
+      // 11.3 us as 8 four-wave workgroups each walking a whole sequence, 7.9 us
+      // as 32 partitions plus the combine).
       const int64_t units = (int64_t)p->batch * c->num_kv_heads;
       const int64_t keys = (int64_t)span * bs;
       part_tokens = units >= 1024 ? 2048
@@ -208,7 +208,8 @@ DecodePlan plan_decode(const pkv_attn_params* p, const pkv_paged_cache* c) {
   plan.valu_waves = 4;
   // A sequence cut into at most 4 partitions is walked by one 16-wave workgroup
   // instead: the same keys per wave and iteration, merged in LDS rather than by
-  // a second kernel over partials (unless the caller asked for partitions).
+  // a second kernel over partials (unless the caller asked for partitions); the
+  // tiny decode then takes 5.4 us with its cache resident, 7.5 us from HBM.
   if (!is_mla(c) && p->split_tokens == 0 && plan.max_np > 1 && plan.max_np <= 4 && span <= kMaxBpp &&
       pkv::decode_valu_wide_supported(c->dtype, c->head_dim, p->num_q_heads / c->num_kv_heads)) {
     plan.bpp = span;

@@ -8,11 +8,13 @@
 // ("KVCache optimisation skill", section 3.1).
 //
 // Work split.  One workgroup (4 waves) owns one (sequence, KV head, partition)
-// where a partition is `blocks_per_part` consecutive table blocks.  All G query
-// heads that share the KV head are processed together, so every K/V row is
-// read from HBM once per step (the GQA sharing of the pages' repeat_kv, done
-// at read time).  Each 16-byte lane chunk holds 8 bf16 (or 4 f32) of a row;
-// LPR = D/8 lanes cover one row, a wave covers 64/LPR rows per load and each
+// where a partition is `blocks_per_part` consecutive table blocks; a call whose
+// sequences would take at most 4 partitions runs one 16-wave workgroup per
+// (sequence, KV head) instead, over the whole sequence.  All G query heads that
+// share the KV head are processed together, so every K/V row is read from HBM
+// once per step (the GQA sharing of the pages' repeat_kv, done at read time).
+// Each 16-byte lane chunk holds 8 bf16 (or 4 f32) of a row; LPR = D / (elements
+// per chunk) lanes cover one row, a wave covers 64/LPR rows per load and each
 // lane keeps U rows of K and of V in flight per iteration.
 //
 // Online softmax (running max m, sum l, rescale by 2^(m_old - m_new)) is kept
