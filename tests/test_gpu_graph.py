@@ -32,6 +32,8 @@ CASES = {
                                                      len_range=(1, 1200), int8=True),
     "fp32 decode (partition kernels)": lambda: workloads.decode_case(7, 3, 8, 2, 128, "f32", block_size=16,
                                                                      max_blocks=50, len_range=(1, 700)),
+    "fp32 decode (one 16-wave workgroup per sequence)": lambda: workloads.decode_case(
+        13, 2, 4, 4, 128, "f32", block_size=128, max_blocks=4, len_range=(1, 512)),
     "MLA decode": lambda: workloads.decode_case(8, 3, 32, 1, 512, "bf16", block_size=64, max_blocks=20,
                                                 len_range=(1, 1200), rope_dim=64, scale=576 ** -0.5),
     "chunked prefill": lambda: workloads.prefill_case(9, 3, 16, 4, 128, "bf16", cached=[100, 0, 700],
@@ -63,6 +65,8 @@ def test_step_replays_in_a_graph(name):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     if "split" in name:
         assert ws_bytes > 0, "this case takes the key split"
+    if "16-wave" in name:
+        assert ws_bytes == 0, "this case takes the whole-sequence workgroups"
     max_q = int(np.diff(case.cu_seqlens_q).max(initial=0)) if case.kind == "prefill" else 1
 
     def step():
