@@ -28,7 +28,7 @@ def _gpu():
     pkv.load()
 
 
-from gpu_util import DeviceCase, as_f64, assert_rows_close, host  # noqa: E402
+from gpu_util import DeviceCase, as_f64, assert_rows_close, dev, host  # noqa: E402
 
 
 # --------------------------------------------------------------------------- prefill
@@ -154,6 +154,39 @@ def test_prefill_single_row_equals_decode(orc):
                                     dec.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     ref, _, _ = oracle_run(orc, dec)
+    assert_rows_close(out_pf, ref, ACC_TOL)
+    assert_rows_close(out_dec, ref, ACC_TOL)
+
+
+@pytest.mark.parametrize("new,window,block_size", [
+    ([40, 17, 5], 0, 64),     # prefill kernel (max_q_len x G = 160 columns)
+    ([40, 17, 5], 150, 16),   # the same with a window over 16-token blocks
+    ([4, 2, 3], 0, 128),      # multi-token decode on the stream split (4 x 4 = 16 columns)
+    ([4, 2, 3], 700, 32),     # the same with a window
+])
+def test_prefill_rows_equal_decode_steps(orc, new, window, block_size):
+    """The "KV Cache notes" minimal implementation's invariant, kernel against kernel: row i
+    of sequence b's chunk (at position p = L_b - n_b + i) equals a decode step whose
+    sequence ends at p, over the same cache and table.  Every new row becomes one decode
+    "sequence" of length p + 1 with sequence b's table row; the decode kernels and the
+    prefill path (prefill kernel or the stream split's multi-token variant) agree within
+    the sum of their fp32-output tolerances, and both match the oracle."""
+    import paged_kv_cache_80_amd as pkv
+    case = workloads.prefill_case(31 + sum(new), 3, 16, 4, 128, "bf16", cached=[300, 0, 1000], new=new,
+                                  block_size=block_size, window=window, null_block=True)
+    d = DeviceCase(case)
+    out_pf, _ = d.run(out_dtype=torch.float32)
+    cu = case.cu_seqlens_q
+    seq_of_row = np.repeat(np.arange(case.B), np.diff(cu)).astype(np.int64)
+    pos = np.concatenate([case.seq_lens[b] - (cu[b + 1] - cu[b]) + np.arange(cu[b + 1] - cu[b])
+                          for b in range(case.B)]).astype(np.int32)
+    bt_rows = d.block_table.index_select(0, torch.from_numpy(seq_of_row).to("cuda"))
+    lens = dev(pos + 1)
+    out_dec = pkv.paged_attn_decode(d.q, d.cache, bt_rows.contiguous(), lens, case.scale, case.window,
+                                    out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_rows_close(out_pf, as_f64(out_dec), 2 * ACC_TOL)
+    ref, _, _ = oracle_run(orc, case)
     assert_rows_close(out_pf, ref, ACC_TOL)
     assert_rows_close(out_dec, ref, ACC_TOL)
 
