@@ -288,6 +288,33 @@ MLA_PREFILL_MATRIX = [
 ]
 
 
+@pytest.mark.parametrize("H,bs,new,window", [
+    (128, 64, [30, 17, 5], 0),    # 128 heads: one 8-wave workgroup per row
+    (48, 16, [30, 17, 5], 90),    # 3 head tiles of 16, a window, 16-token blocks
+])
+def test_mla_prefill_rows_equal_decode_steps(orc, H, bs, new, window):
+    """MLA form of the prefill-equals-decode invariant, kernel against kernel: every new row
+    of the chunk equals an MLA decode step whose sequence ends at that row's position,
+    over the same latent cache and table; both match the oracle."""
+    import paged_kv_cache_80_amd as pkv
+    case = workloads.prefill_case(77 + H, 3, H, 1, 512, "bf16", cached=[300, 0, 700], new=new, block_size=bs,
+                                  window=window, null_block=True, rope_dim=64, scale=1.0 / np.sqrt(576.0))
+    d = DeviceCase(case)
+    out_pf, _ = d.run(out_dtype=torch.float32)
+    cu = case.cu_seqlens_q
+    seq_of_row = np.repeat(np.arange(case.B), np.diff(cu)).astype(np.int64)
+    pos = np.concatenate([case.seq_lens[b] - (cu[b + 1] - cu[b]) + np.arange(cu[b + 1] - cu[b])
+                          for b in range(case.B)]).astype(np.int32)
+    bt_rows = d.block_table.index_select(0, torch.from_numpy(seq_of_row).to("cuda")).contiguous()
+    out_dec = pkv.paged_attn_decode(d.q, d.cache, bt_rows, dev(pos + 1), case.scale, case.window,
+                                    q_rope=d.q_rope, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_rows_close(out_pf, as_f64(out_dec), 2 * ACC_TOL)
+    ref, _, _ = oracle_run(orc, case)
+    assert_rows_close(out_pf, ref, ACC_TOL)
+    assert_rows_close(out_dec, ref, ACC_TOL)
+
+
 @pytest.mark.parametrize("shape", MLA_PREFILL_MATRIX)
 def test_mla_prefill_matches_oracle(orc, shape):
     B, H, bs, cached, new, w = shape
