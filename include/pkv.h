@@ -101,7 +101,9 @@ typedef struct {
   int32_t window;             /* 0 = full attention; W > 0: a query at position p sees keys  */
                               /* p-W < j <= p ("KV Cache notes", sliding-window section)     */
   int32_t out_dtype;          /* pkv_dtype of `out` (f32 out is a diagnostic mode)           */
-  int32_t split_tokens;       /* decode only, a multiple of block_size; 0 = library choice.  */
+  int32_t split_tokens;       /* decode only, a multiple of block_size; 0 = library choice   */
+                              /* (which for small f32 / head_dim != 128 calls may be one     */
+                              /* workgroup per whole sequence, needing no workspace).        */
                               /* Partition kernels (f32, head_dim != 128, MLA): keys per     */
                               /* workgroup partition.  Stream-split kernel (bf16, head_dim   */
                               /* 128): the fewest keys one wave group streams, which caps    */
